@@ -1,0 +1,199 @@
+/*
+ * nvfp4mi.h - C ABI of the MI355X (gfx950) NVFP4 post-training-quantization
+ * hot path.
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 elements {0, +-0.5, +-1, +-1.5, +-2,
+ * +-3, +-4, +-6}, one non-negative E4M3FN block scale per 16 consecutive
+ * elements along the input-channel axis, and one FP32 tensor scale scale_2.
+ * The value of element i of block b is e2m1(i) * RN_f32(e4m3(code_b) *
+ * scale_2), cast to BF16 for use ("Coder390 NVFP4 校正（校准）方式" §2, format
+ * paragraph; "NVFP4 量化流程说明" §2.2, §5.4).
+ *
+ * Common conventions
+ * ------------------
+ * - Every pointer argument is a DEVICE pointer (hipMalloc'ed or from a
+ *   framework allocator) owned by the caller, unless stated otherwise.  The
+ *   library keeps no pointer after a call returns and never allocates device
+ *   memory; scratch memory comes in as a caller-provided workspace.
+ * - bf16 values are passed as uint16_t bit patterns.  Matrices are row-major;
+ *   "ld" arguments are row strides in ELEMENTS.  Blocks of 16 run along the
+ *   last (contiguous) axis.
+ * - Packed E2M1 data: two codes per byte, element 2i in bits 0-3 and element
+ *   2i+1 in bits 4-7; bit 3 of a code is the sign.  Block scales: one E4M3FN
+ *   byte per block, row-major [rows][k/16].
+ * - stream is a hipStream_t passed as void* (NULL = the default stream).  All
+ *   work is enqueued on it asynchronously; outputs are valid once the stream
+ *   has synchronised.  Kernel faults surface at that synchronisation.
+ * - Arguments are validated on the host BEFORE any HIP call; on a validation
+ *   error nothing is enqueued.  Functions return NVFP4_OK (0) or one of the
+ *   NVFP4_ERR_* codes below; nvfp4_status_string() describes a code (for
+ *   NVFP4_ERR_HIP it includes the HIP error text of the failing call on the
+ *   calling thread).
+ * - Buffers must not overlap unless stated (the cast rewrites its nibbles in
+ *   place by design).  Calls are reentrant; concurrent calls must not share
+ *   outputs or workspaces.
+ * - Inputs are expected to be finite.  NaN/Inf inputs give unspecified codes.
+ *
+ * Rounding (readings of the pages, which name no rounding mode): every
+ * encode rounds the exact real quotient once to nearest, ties to even, and
+ * saturates at the format's largest finite value (6 for E2M1, 448 for E4M3);
+ * a negative element that rounds to zero keeps its sign bit.
+ */
+#ifndef NVFP4MI_H
+#define NVFP4MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL_ARG = 1,     /* a required pointer is NULL                         */
+  NVFP4_ERR_BAD_SHAPE = 2,    /* a size is negative, k % 16 != 0 (k % 32 for the
+                                 cast), ld < k, or a product overflows int64       */
+  NVFP4_ERR_MISALIGNED = 3,   /* a bf16/byte matrix row is not 16-byte aligned       */
+  NVFP4_ERR_WORKSPACE = 4,    /* workspace smaller than the matching *_bytes() query */
+  NVFP4_ERR_BAD_INPUT = 5,    /* an argument value is out of range (e.g. mats <= 0)  */
+  NVFP4_ERR_HIP = 6           /* a HIP launch or API call failed                     */
+};
+
+/* Text for a status code (static storage; for NVFP4_ERR_HIP the text of the
+ * last HIP error seen on the calling thread). */
+const char* nvfp4_status_string(int status);
+
+/*
+ * Step 1 of the per-Linear calibration, max calibration ("Coder390 NVFP4
+ * 校正（校准）方式" §2 step 1), with the tensor-scale formula of "NVFP4
+ * 量化流程说明" §3.4: amax = max |x| over n bf16 values and
+ * scale_2 = RN_f32(amax / (6 * 448)).
+ *
+ * x          [n] bf16, contiguous, 16-byte aligned (n may be 0: amax = 0).
+ * scale2_out device float[1]: receives scale_2.  Also used as the running
+ *            accumulator, so it must not alias x.
+ * amax_out   device float[1] or NULL: receives amax.
+ * Errors: NULL_ARG (x with n > 0, scale2_out), BAD_SHAPE (n < 0),
+ *         MISALIGNED (x), HIP.
+ */
+int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out,
+                         float* amax_out, void* stream);
+
+/*
+ * Bytes of workspace nvfp4_hessian_accum needs for (tokens, k); 0 when
+ * tokens == 0.  Returns 0 for invalid sizes too (the accumulate call then
+ * reports the shape error).
+ */
+size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k);
+
+/*
+ * Step 2, the local block-diagonal Hessian ("Coder390 NVFP4 校正（校准）方式"
+ * §2 step 2): for every group g of 16 input channels,
+ *   H[g] += sum_t x[t, 16g:16g+16]^T x[t, 16g:16g+16]
+ * over the `tokens` rows of x, accumulated into H IN PLACE so a calibration
+ * stream can be fed chunk by chunk.  Products of bf16 values are exact in
+ * fp32; partial sums run in fp32 on MFMA over at most a few thousand tokens
+ * and are then reduced in fp64 in a fixed order (bitwise reproducible).
+ *
+ * x          [tokens][ldx] bf16; columns 0..k-1 are used.
+ * H          [k/16][16][16] float, in/out.
+ * amax_inout device float[1] or NULL: if given, it is raised to
+ *            max(*amax_inout, max |x|) (step 1 fused into the same read of x).
+ * workspace  device buffer of at least nvfp4_hessian_workspace_bytes(tokens, k)
+ *            bytes (may be NULL when that is 0); contents are scratch.
+ * Errors: NULL_ARG, BAD_SHAPE (tokens < 0, k <= 0, k % 16, ldx < k),
+ *         MISALIGNED (x or ldx not 16-byte aligned rows), WORKSPACE, HIP.
+ */
+int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
+                        float* H, float* amax_inout, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Step 3, the Hessian-weighted block-scale sweep (fp8_scale_sweep,
+ * "Coder390 NVFP4 校正（校准）方式" §2 step 3).  For every block b = (row r,
+ * group g) of 16 weights w and every finite E4M3 code c in 0x00..0x7E:
+ *   d_c  = RN_f32(e4m3(c) * scale_2)
+ *   q    = E2M1 quantization of w / d_c (exact quotient, RNE, saturating;
+ *          d_c = 0 quantizes to zero)
+ *   cost = (w - q*d_c)^T H[g] (w - q*d_c)
+ * and the code of least cost is kept (lowest code on ties).  Costs are
+ * evaluated in fp32 (MFMA); the quantization itself is exact.
+ *
+ * w       [rows][ldw] bf16, columns 0..k-1 (W of an nn.Linear: [out][in]).
+ * H       [k/16][16][16] float (from nvfp4_hessian_accum).
+ * scale2  device float[1]: scale_2 of w (from nvfp4_compute_scale2).
+ * packed  [rows][k/2] uint8 out: nibbles at the chosen codes.
+ * codes   [rows][k/16] uint8 out: chosen E4M3 codes.
+ * cost    [rows][k/16] float out or NULL: the fp32 cost of the chosen code.
+ * Errors: NULL_ARG, BAD_SHAPE (rows < 0, k <= 0, k % 16, ldw < k),
+ *         MISALIGNED (w rows), HIP.
+ */
+int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw,
+                      const float* H, const float* scale2, uint8_t* packed,
+                      uint8_t* codes, float* cost, void* stream);
+
+/*
+ * Dynamic per-16 NVFP4 activation quantizer ("NVFP4 量化流程说明" §3.4-§3.5):
+ * per block, amax_b = max |x| over the 16 elements, code =
+ * RNE_sat(amax_b / (6 * scale_2)) on the E4M3 grid (raised to 0x01 if the
+ * block is nonzero and that gives 0x00), then E2M1 quantization of every
+ * element at d = RN_f32(e4m3(code) * scale_2).  One pass over x.
+ *
+ * x       [rows][ldx] bf16, columns 0..k-1.
+ * scale2  device float[1]: the per-tensor scale (calibrated or from
+ *         nvfp4_compute_scale2); 0 quantizes everything to zero.
+ * packed  [rows][k/2] uint8 out;  codes [rows][k/16] uint8 out.
+ * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED, HIP.
+ */
+int nvfp4_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                           const float* scale2, uint8_t* packed, uint8_t* codes,
+                           void* stream);
+
+/*
+ * Two-DequantizeLinear chain ("NVFP4 量化流程说明" §5.4): DQ1 d =
+ * RN_f32(e4m3(code) * scale_2), DQ2 y = RN_f32(e2m1 * d), then a cast to
+ * BF16 (nearest even).  Code 0x7F (NaN) gives NaN outputs.
+ *
+ * packed [rows][k/2] uint8, contiguous; codes [rows][k/16] uint8, contiguous;
+ * scale2 device float[1];  out [rows][k] bf16, contiguous.
+ * Errors: NULL_ARG, BAD_SHAPE (rows < 0, k <= 0, k % 16), MISALIGNED, HIP.
+ */
+int nvfp4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2,
+                  int64_t rows, int64_t k, uint16_t* out, void* stream);
+
+/*
+ * Closed-form MXFP4 -> NVFP4 cast ("从MXFP4到NVFP4：Model Optimizer混合精度格式
+ * 转换完全攻略" §2-§3; "从校准到导出：DeepSeek-V4-Pro-0813-nvfp4-DSpark
+ * 三阶段 NVFP4 量化流程实战", export stage).  The input holds `groups` groups of
+ * `mats_per_group` MXFP4 matrices (e.g. an expert's w1 and w3) that share one
+ * NVFP4 scale_2.  Per group, with k_j = e8m0_j - 127 and k_max its maximum:
+ *   scale_2 = 2^(k_max - 8)             (global_amax = 6 * 448 * 2^(k_max - 8))
+ *   MX block j with k_max - k_j <= 17:  both NVFP4 blocks get the E4M3 code of
+ *                                       2^(k_j - k_max + 8); nibbles untouched
+ *   otherwise (fallback):               each 16-element half is requantized from
+ *                                       its data with the dynamic quantizer's
+ *                                       rule (block amax, code raised to 0x01)
+ * E8M0 code 255 (NaN) is left out of k_max; its blocks get code 0x7F (NaN)
+ * and keep their nibbles.
+ *
+ * packed   [groups][mats][rows][k/2] uint8, IN/OUT: only fallback blocks are
+ *          rewritten.
+ * e8m0     [groups][mats][rows][k/32] uint8.
+ * codes_out  [groups][mats][rows][k/16] uint8 out.
+ * scale2_out [groups] float out (also used as scratch during the call).
+ * fallback_blocks_out [groups] int64 out or NULL: number of 32-element MX
+ *          blocks per group that took the fallback (0 = lossless group).
+ * Errors: NULL_ARG, BAD_SHAPE (sizes <= 0, k % 32), BAD_INPUT, MISALIGNED
+ *         (packed/e8m0/codes_out not 16-byte aligned), HIP.
+ */
+int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups,
+                        int64_t mats_per_group, int64_t rows, int64_t k,
+                        uint8_t* codes_out, float* scale2_out,
+                        int64_t* fallback_blocks_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MI_H */

@@ -1,0 +1,219 @@
+"""NVFP4 post-training quantization on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libnvfp4mi.so (include/nvfp4mi.h).  Every step runs
+in the HIP kernels of that library; this module only checks tensor dtypes,
+devices and layouts, allocates outputs with torch, and passes pointers and
+the current HIP stream.  It fails loudly when the library is missing.
+
+Functions (names as in the C ABI):
+  compute_scale2(x)                         -> (scale2[1] f32, amax[1] f32)
+  hessian_accum(x, H, amax=None, workspace=None)   H += block-diag X^T X (in place)
+  scale_sweep(w, H, scale2, want_cost=False) -> (packed u8, codes u8, cost f32 | None)
+  quantize_dynamic(x, scale2)               -> (packed u8, codes u8)
+  dequant(packed, codes, scale2)            -> bf16
+  mxfp4_to_nvfp4_cast(packed, e8m0, want_fallback=True) -> (codes, scale2, fallback)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
+    "hessian_accum", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "nvfp4_compute_scale2": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "nvfp4_hessian_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "nvfp4_hessian_accum": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                           ctypes.c_size_t, _c_void_p]),
+    "nvfp4_scale_sweep": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_void_p, _c_void_p]),
+    "nvfp4_quantize_dynamic": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                              _c_void_p]),
+    "nvfp4_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
+    "mxfp4_to_nvfp4_cast": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                           _c_void_p, _c_void_p]),
+}
+
+_lib = None
+
+
+class NvFp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libnvfp4mi.so (built by nvfp4_post_quantization_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m nvfp4_post_quantization_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        text = load().nvfp4_status_string(status).decode(errors="replace")
+        raise NvFp4Error(fn, status, text)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str, dims: int | None = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions (got {t.dim()})")
+    return t
+
+
+def _row_major(t: torch.Tensor, name: str) -> int:
+    """Row stride of a 2-D tensor whose rows are contiguous."""
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    return t.stride(0) if t.size(0) > 1 else t.size(1)
+
+
+def compute_scale2(x: torch.Tensor):
+    """Tensor amax and scale_2 = amax / (6 * 448) of a contiguous bf16 tensor."""
+    _dev(x, torch.bfloat16, "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    s2 = torch.empty(1, dtype=torch.float32, device=x.device)
+    am = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check("nvfp4_compute_scale2",
+           load().nvfp4_compute_scale2(x.data_ptr(), x.numel(), s2.data_ptr(), am.data_ptr(), _stream(x)))
+    return s2, am
+
+
+def hessian_workspace_bytes(tokens: int, k: int) -> int:
+    return int(load().nvfp4_hessian_workspace_bytes(tokens, k))
+
+
+def hessian_accum(x: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """H[k/16,16,16] (f32) += block-diagonal X^T X of bf16 x[tokens, k]; in place.
+
+    amax (f32[1]) is raised to max(amax, max|x|) when given.  workspace is a
+    uint8 tensor of at least hessian_workspace_bytes(tokens, k) bytes
+    (allocated here when omitted).
+    """
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(H, torch.float32, "H")
+    tokens, k = x.shape
+    if H.numel() != (k // 16) * 256 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [k/16, 16, 16] tensor")
+    ldx = _row_major(x, "x")
+    need = hessian_workspace_bytes(tokens, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    if amax is not None:
+        _dev(amax, torch.float32, "amax")
+    _check("nvfp4_hessian_accum", load().nvfp4_hessian_accum(
+        x.data_ptr(), tokens, k, ldx, H.data_ptr(), amax.data_ptr() if amax is not None else None,
+        workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return H
+
+
+def scale_sweep(w: torch.Tensor, H: torch.Tensor, scale2: torch.Tensor, want_cost: bool = False,
+                out=None):
+    """Hessian-weighted sweep of the E4M3 block scale of bf16 w[rows, k]."""
+    _dev(w, torch.bfloat16, "w", 2)
+    _dev(H, torch.float32, "H")
+    _dev(scale2, torch.float32, "scale2")
+    rows, k = w.shape
+    if H.numel() != (k // 16) * 256 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [k/16, 16, 16] tensor")
+    ldw = _row_major(w, "w")
+    if out is None:
+        packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=w.device)
+        codes = torch.empty((rows, k // 16), dtype=torch.uint8, device=w.device)
+        cost = torch.empty((rows, k // 16), dtype=torch.float32, device=w.device) if want_cost else None
+    else:
+        packed, codes, cost = out
+    _check("nvfp4_scale_sweep", load().nvfp4_scale_sweep(
+        w.data_ptr(), rows, k, ldw, H.data_ptr(), scale2.data_ptr(), packed.data_ptr(), codes.data_ptr(),
+        cost.data_ptr() if cost is not None else None, _stream(w)))
+    return packed, codes, cost
+
+
+def quantize_dynamic(x: torch.Tensor, scale2: torch.Tensor, out=None):
+    """Dynamic per-16 NVFP4 quantization of bf16 x[rows, k]."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(scale2, torch.float32, "scale2")
+    rows, k = x.shape
+    ldx = _row_major(x, "x")
+    if out is None:
+        packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device)
+    else:
+        packed, codes = out
+    _check("nvfp4_quantize_dynamic", load().nvfp4_quantize_dynamic(
+        x.data_ptr(), rows, k, ldx, scale2.data_ptr(), packed.data_ptr(), codes.data_ptr(), _stream(x)))
+    return packed, codes
+
+
+def dequant(packed: torch.Tensor, codes: torch.Tensor, scale2: torch.Tensor, out=None) -> torch.Tensor:
+    """bf16[rows, k] from NVFP4 (packed u8 [rows, k/2], codes u8 [rows, k/16])."""
+    _dev(packed, torch.uint8, "packed", 2)
+    _dev(codes, torch.uint8, "codes", 2)
+    _dev(scale2, torch.float32, "scale2")
+    rows, kh = packed.shape
+    k = kh * 2
+    if not (packed.is_contiguous() and codes.is_contiguous()) or codes.shape != (rows, k // 16):
+        raise ValueError("packed/codes must be contiguous [rows, k/2] / [rows, k/16]")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.bfloat16, device=packed.device)
+    _check("nvfp4_dequant", load().nvfp4_dequant(
+        packed.data_ptr(), codes.data_ptr(), scale2.data_ptr(), rows, k, out.data_ptr(), _stream(packed)))
+    return out
+
+
+def mxfp4_to_nvfp4_cast(packed: torch.Tensor, e8m0: torch.Tensor, want_fallback: bool = True, out=None):
+    """Cast MXFP4 [groups, mats, rows, k/2] (+ E8M0 [.., k/32]) to NVFP4 in place.
+
+    Returns (codes u8 [groups, mats, rows, k/16], scale2 f32 [groups],
+    fallback int64 [groups] | None); packed is rewritten only where a block
+    falls outside the exact window.
+    """
+    _dev(packed, torch.uint8, "packed", 4)
+    _dev(e8m0, torch.uint8, "e8m0", 4)
+    g, m, r, kh = packed.shape
+    k = kh * 2
+    if e8m0.shape != (g, m, r, k // 32) or not (packed.is_contiguous() and e8m0.is_contiguous()):
+        raise ValueError("e8m0 must be contiguous [groups, mats, rows, k/32] matching packed")
+    if out is None:
+        codes = torch.empty((g, m, r, k // 16), dtype=torch.uint8, device=packed.device)
+        s2 = torch.empty(g, dtype=torch.float32, device=packed.device)
+        fb = torch.empty(g, dtype=torch.int64, device=packed.device) if want_fallback else None
+    else:
+        codes, s2, fb = out
+    _check("mxfp4_to_nvfp4_cast", load().mxfp4_to_nvfp4_cast(
+        packed.data_ptr(), e8m0.data_ptr(), g, m, r, k, codes.data_ptr(), s2.data_ptr(),
+        fb.data_ptr() if fb is not None else None, _stream(packed)))
+    return codes, s2, fb

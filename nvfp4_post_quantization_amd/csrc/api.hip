@@ -1,0 +1,133 @@
+// C ABI entry points (include/nvfp4mi.h): argument validation on the host,
+// then the launches.  No HIP call happens before validation succeeds, so
+// every error code except NVFP4_ERR_HIP can be produced without a GPU.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.hpp"
+
+namespace nvfp4 {
+
+static thread_local char g_hip_error[256] = "no HIP error recorded";
+
+void set_hip_error(hipError_t e, const char* where) {
+  snprintf(g_hip_error, sizeof g_hip_error, "HIP error in %s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+int force_exact_flag() {
+  const char* v = getenv("NVFP4MI_FORCE_EXACT");
+  return (v && v[0] && v[0] != '0') ? 1 : 0;
+}
+
+// a * b <= INT64_MAX for non-negative a, b
+static bool mul_fits(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
+
+// [rows][ld] matrix of `elem` bytes with `cols` used columns.
+static int check_matrix(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  if (rows < 0 || cols <= 0 || ld < cols) return NVFP4_ERR_BAD_SHAPE;
+  if (!mul_fits(rows, ld) || !mul_fits(rows * ld, elem)) return NVFP4_ERR_BAD_SHAPE;
+  return NVFP4_OK;
+}
+
+static int check_bf16_rows(const void* p, int64_t ld) {
+  if (!aligned16(p) || (ld % 8) != 0) return NVFP4_ERR_MISALIGNED;
+  return NVFP4_OK;
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case NVFP4_ERR_BAD_SHAPE: return "bad shape: negative size, k not a multiple of the block, ld < k, or size overflow";
+    case NVFP4_ERR_MISALIGNED: return "misaligned buffer: rows must start on 16-byte boundaries";
+    case NVFP4_ERR_WORKSPACE: return "workspace smaller than the size the matching *_bytes query returns";
+    case NVFP4_ERR_BAD_INPUT: return "argument value out of range";
+    case NVFP4_ERR_HIP: return g_hip_error;
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, void* stream) {
+  if (n < 0 || !mul_fits(n, 2)) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale2_out || (n > 0 && !x)) return NVFP4_ERR_NULL_ARG;
+  if (n > 0 && !aligned16(x)) return NVFP4_ERR_MISALIGNED;
+  return launch_compute_scale2(x, n, scale2_out, amax_out, as_stream(stream));
+}
+
+size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k) {
+  if (tokens <= 0 || k <= 0 || (k % 16) != 0) return 0;
+  return hessian_workspace_bytes(tokens, k);
+}
+
+int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax_inout,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_matrix(tokens, k, ldx, 2);
+  if (st) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL_ARG;
+  if (tokens == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx))) return st;
+  size_t need = hessian_workspace_bytes(tokens, k);
+  if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (need && !workspace) return NVFP4_ERR_NULL_ARG;
+  return launch_hessian_accum(x, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
+}
+
+int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
+                      uint8_t* packed, uint8_t* codes, float* cost, void* stream) {
+  int st = check_matrix(rows, k, ldw, 2);
+  if (st) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!H || !scale2 || ((!w || !packed || !codes) && rows > 0)) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(w, ldw))) return st;
+  return launch_scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, as_stream(stream));
+}
+
+int nvfp4_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
+                           uint8_t* packed, uint8_t* codes, void* stream) {
+  int st = check_matrix(rows, k, ldx, 2);
+  if (st) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale2 || ((!x || !packed || !codes) && rows > 0)) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx))) return st;
+  if (!aligned16(packed)) return NVFP4_ERR_MISALIGNED;
+  return launch_quantize_dynamic(x, rows, k, ldx, scale2, packed, codes, as_stream(stream));
+}
+
+int nvfp4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2, int64_t rows, int64_t k,
+                  uint16_t* out, void* stream) {
+  int st = check_matrix(rows, k, k, 2);
+  if (st) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale2 || ((!packed || !codes || !out) && rows > 0)) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if (!aligned16(packed) || !aligned16(out)) return NVFP4_ERR_MISALIGNED;
+  return launch_dequant(packed, codes, scale2, rows, k, out, as_stream(stream));
+}
+
+int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats_per_group,
+                        int64_t rows, int64_t k, uint8_t* codes_out, float* scale2_out,
+                        int64_t* fallback_blocks_out, void* stream) {
+  if (groups < 0 || rows < 0 || k <= 0 || (k % 32) != 0) return NVFP4_ERR_BAD_SHAPE;
+  if (mats_per_group <= 0) return NVFP4_ERR_BAD_INPUT;
+  if (!mul_fits(groups, mats_per_group) || !mul_fits(groups * mats_per_group, rows) ||
+      !mul_fits(groups * mats_per_group * rows, k))
+    return NVFP4_ERR_BAD_SHAPE;
+  if (groups == 0) return NVFP4_OK;
+  if (!scale2_out) return NVFP4_ERR_NULL_ARG;
+  if (rows > 0 && (!packed || !e8m0 || !codes_out)) return NVFP4_ERR_NULL_ARG;
+  if (rows > 0 && (!aligned16(packed) || !aligned16(e8m0) || !aligned16(codes_out))) return NVFP4_ERR_MISALIGNED;
+  return launch_mx_cast(packed, e8m0, groups, mats_per_group, rows, k, codes_out, scale2_out,
+                        fallback_blocks_out, as_stream(stream));
+}
+
+}  // extern "C"

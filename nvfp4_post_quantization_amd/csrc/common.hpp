@@ -1,0 +1,47 @@
+// Host-side helpers shared by the launchers: status codes, HIP error capture.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/nvfp4mi.h"
+
+namespace nvfp4 {
+
+// Remembers the text of the last failing HIP call on this thread.
+void set_hip_error(hipError_t e, const char* where);
+
+inline int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return NVFP4_OK;
+  set_hip_error(e, where);
+  return NVFP4_ERR_HIP;
+}
+
+inline int launch_status(const char* where) { return hip_status(hipGetLastError(), where); }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// NVFP4MI_FORCE_EXACT=1 in the environment disables the certified FP4-convert
+// fast path so that tests can exercise the exact threshold path everywhere.
+int force_exact_flag();
+
+// Workgroups that keep every CU busy for streaming kernels (8 per CU).
+constexpr int kStreamGrid = 256 * 8;
+
+// Launchers (one per kernel family); arguments are validated by the caller.
+int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, hipStream_t s);
+int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
+                            uint8_t* packed, uint8_t* codes, hipStream_t s);
+int launch_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2, int64_t rows, int64_t k,
+                   uint16_t* out, hipStream_t s);
+size_t hessian_workspace_bytes(int64_t tokens, int64_t k);
+int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
+                         void* workspace, hipStream_t s);
+int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
+                       const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s);
+int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,
+                   uint8_t* codes, float* scale2, int64_t* fallback, hipStream_t s);
+
+}  // namespace nvfp4

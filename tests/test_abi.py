@@ -1,0 +1,119 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call.
+
+Pointers used here are never dereferenced: every call is built to fail
+validation (a call that passed it would launch kernels).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_post_quantization_amd as nq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4mi.h")
+
+OK, NULL, SHAPE, ALIGN, WS, BADIN, HIP = 0, 1, 2, 3, 4, 5, 6
+P = 0x10000          # a 16-byte-aligned fake address (never dereferenced)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nq.LIB_PATH):
+        pytest.skip("libnvfp4mi.so not built")
+    return nq.load()
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert set(names) == {
+        "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
+        "nvfp4_hessian_accum", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
+        "mxfp4_to_nvfp4_cast",
+    }
+    for n in names:
+        assert hasattr(lib, n), n
+    raw = ctypes.CDLL(nq.LIB_PATH)
+    for n in names:
+        getattr(raw, n)
+
+
+def test_status_strings(lib):
+    for s in range(0, 7):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_status_string(0) == b"ok"
+    assert b"unknown" in lib.nvfp4_status_string(99)
+
+
+def test_compute_scale2_validation(lib):
+    assert lib.nvfp4_compute_scale2(P, -1, P, None, None) == SHAPE
+    assert lib.nvfp4_compute_scale2(None, 16, P, None, None) == NULL
+    assert lib.nvfp4_compute_scale2(P, 16, None, None, None) == NULL
+    assert lib.nvfp4_compute_scale2(P + 2, 16, P, None, None) == ALIGN
+
+
+def test_hessian_validation(lib):
+    ws = lib.nvfp4_hessian_workspace_bytes(65536, 4096)
+    assert ws > 0 and ws % 1024 == 0
+    assert lib.nvfp4_hessian_workspace_bytes(0, 4096) == 0
+    assert lib.nvfp4_hessian_workspace_bytes(16, 24) == 0
+    f = lib.nvfp4_hessian_accum
+    assert f(P, 16, 24, 24, P, None, P, 1 << 20, None) == SHAPE           # k % 16
+    assert f(P, 16, 32, 16, P, None, P, 1 << 20, None) == SHAPE           # ld < k
+    assert f(P, -1, 32, 32, P, None, P, 1 << 20, None) == SHAPE
+    assert f(P, 16, 0, 0, P, None, P, 1 << 20, None) == SHAPE
+    assert f(P, 16, 32, 32, None, None, P, 1 << 20, None) == NULL
+    assert f(None, 16, 32, 32, P, None, P, 1 << 20, None) == NULL
+    assert f(P + 2, 16, 32, 32, P, None, P, 1 << 20, None) == ALIGN
+    assert f(P, 16, 32, 36, P, None, P, 1 << 20, None) == ALIGN           # row stride not 16 B
+    need = lib.nvfp4_hessian_workspace_bytes(16, 32)
+    assert f(P, 16, 32, 32, P, None, P, need - 1, None) == WS
+    assert f(P, 16, 32, 32, P, None, None, need, None) == NULL
+    assert f(P, 0, 32, 32, P, None, None, 0, None) == OK                  # nothing to do
+    assert f(P, 1 << 62, 32, 1 << 40, P, None, P, 1 << 20, None) == SHAPE   # overflow
+
+
+def test_sweep_quant_dequant_validation(lib):
+    s = lib.nvfp4_scale_sweep
+    assert s(P, 4, 24, 24, P, P, P, P, None, None) == SHAPE
+    assert s(P, 4, 32, 32, None, P, P, P, None, None) == NULL
+    assert s(P, 4, 32, 32, P, None, P, P, None, None) == NULL
+    assert s(P, 4, 32, 32, P, P, None, P, None, None) == NULL
+    assert s(P + 8, 4, 32, 32, P, P, P, P, None, None) == ALIGN
+    assert s(P, 0, 32, 32, P, P, P, P, None, None) == OK
+    qd = lib.nvfp4_quantize_dynamic
+    assert qd(P, 4, 40, 40, P, P, P, None) == SHAPE
+    assert qd(P, 4, 32, 32, None, P, P, None) == NULL
+    assert qd(P + 4, 4, 32, 32, P, P, P, None) == ALIGN
+    assert qd(P, 4, 32, 32, P, P + 1, P, None) == ALIGN
+    dq = lib.nvfp4_dequant
+    assert dq(P, P, P, 4, 8, P, None) == SHAPE
+    assert dq(P, None, P, 4, 32, P, None) == NULL
+    assert dq(P, P, P, 4, 32, P + 2, None) == ALIGN
+    assert dq(P, P, P, 0, 32, P, None) == OK
+
+
+def test_cast_validation(lib):
+    c = lib.mxfp4_to_nvfp4_cast
+    assert c(P, P, 2, 2, 4, 48, P, P, None, None) == SHAPE        # k % 32
+    assert c(P, P, -1, 2, 4, 64, P, P, None, None) == SHAPE
+    assert c(P, P, 2, 0, 4, 64, P, P, None, None) == BADIN
+    assert c(P, P, 2, 2, 4, 64, P, None, None, None) == NULL
+    assert c(None, P, 2, 2, 4, 64, P, P, None, None) == NULL
+    assert c(P, P + 1, 2, 2, 4, 64, P, P, None, None) == ALIGN
+    assert c(P, P, 0, 2, 4, 64, P, P, None, None) == OK
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nq.quantize_dynamic(x, torch.zeros(1))

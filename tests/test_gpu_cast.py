@@ -1,0 +1,64 @@
+"""GPU parity: closed-form MXFP4 -> NVFP4 cast against the oracle, bit for bit
+(codes, rewritten nibbles, scale_2, fallback counts)."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import mxcast as M
+import nvfp4_post_quantization_amd as nq
+
+from _gpu import DEV, need_gpu, note, to_dev_u8, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _check(packed, e8):
+    p_dev = to_dev_u8(packed)
+    codes, s2, fb = nq.mxfp4_to_nvfp4_cast(p_dev, to_dev_u8(e8))
+    p_ref, c_ref, s2_ref, fb_ref = M.mxfp4_to_nvfp4(packed, e8)
+    assert np.array_equal(host(codes), c_ref)
+    assert np.array_equal(host(s2).astype(np.float64), s2_ref)
+    assert np.array_equal(host(fb), fb_ref)
+    assert np.array_equal(host(p_dev), p_ref)
+    return fb_ref
+
+
+@pytest.mark.parametrize("seed,experts,rows,k,frac", [(0, 4, 64, 512, 0.01), (1, 3, 16, 7168, 0.005),
+                                                      (2, 2, 8, 256, 0.2)])
+def test_cast_small(seed, experts, rows, k, frac):
+    note(f"cast seed={seed} experts={experts} rows={rows} k={k}")
+    packed, e8, forced = datagen.config5(seed=seed, experts=experts, rows=rows, k=k, forced_frac=frac)
+    fb = _check(packed, e8)
+    assert np.array_equal(fb, forced.reshape(experts, -1).sum(axis=1))
+
+
+def test_cast_generic_path_and_nan():
+    """Groups whose block count is not a multiple of 4 (scalar path) and a NaN exponent."""
+    note("cast generic path + NaN exponent")
+    rng = np.random.default_rng(3)
+    g, m, r, k = 5, 1, 3, 32
+    packed = rng.integers(0, 256, (g, m, r, k // 2)).astype(np.uint8)
+    e8 = (127 + rng.integers(-30, 10, (g, m, r, k // 32))).astype(np.uint8)
+    e8[1, 0, 1, 0] = 255
+    e8[2, 0, :, 0] = 255                  # a group with no valid exponent at all
+    _check(packed, e8)
+
+
+def test_cast_zero_halves_and_extremes():
+    note("cast zero halves and extreme exponents")
+    rng = np.random.default_rng(4)
+    g, m, r, k = 2, 2, 4, 64
+    packed = rng.integers(0, 256, (g, m, r, k // 2)).astype(np.uint8)
+    packed[0, 0, 0, :8] &= 0x88           # a half with zero magnitudes (signs kept)
+    e8 = np.full((g, m, r, k // 32), 127, np.uint8)
+    e8[0, 0, 0, 0] = 60                   # far below k_max: fallback
+    e8[0, 1, 2, 1] = 254                  # k_max = 127
+    e8[1] = rng.integers(0, 30, (m, r, k // 32)).astype(np.uint8)   # tiny exponents
+    e8[1, 0, 0, 0] = 0
+    _check(packed, e8)

@@ -1,0 +1,136 @@
+"""GPU parity: tensor scale, dynamic NVFP4 quantizer and the two-DQ dequant
+against the oracle, bit for bit.  Inputs from datagen; expected values from
+the oracle only."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from oracle import formats as F
+from oracle import nvfp4 as N
+import nvfp4_post_quantization_amd as nq
+
+from _gpu import DEV, need_gpu, note, to_dev_bf16, to_host_bits, to_dev_u8, to_dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.fixture(params=["fast", "exact"])
+def path(request, monkeypatch):
+    if request.param == "exact":
+        monkeypatch.setenv("NVFP4MI_FORCE_EXACT", "1")
+    else:
+        monkeypatch.delenv("NVFP4MI_FORCE_EXACT", raising=False)
+    return request.param
+
+
+def _check_scale2(bits: np.ndarray):
+    x = to_dev_bf16(bits.reshape(-1))
+    s2, am = nq.compute_scale2(x)
+    amax, s2_ref = N.tensor_scale(bits)
+    assert float(host(am)[0]) == amax
+    assert float(host(s2)[0]) == s2_ref
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4095, 65536 + 3])
+def test_scale2_sizes(n):
+    note(f"compute_scale2 n={n}")
+    rng = np.random.default_rng(n)
+    bits = datagen.f32_to_bf16_bits((rng.standard_normal(n) * 3).astype(np.float32))
+    if n:
+        bits[rng.integers(0, n)] = datagen.f32_to_bf16_bits(np.array([-517.0], np.float32))[0]
+    _check_scale2(bits)
+
+
+def test_scale2_configs():
+    w1, x1 = datagen.config1()
+    w2, _ = datagen.config2()
+    note("compute_scale2 configs 1-3")
+    for b in (w1, x1, w2, datagen.config3()):
+        _check_scale2(b)
+
+
+def _quant_case(bits2d: np.ndarray, s2: float, ld: int | None = None):
+    rows, k = bits2d.shape
+    if ld is None:
+        x = to_dev_bf16(bits2d)
+    else:
+        full = np.zeros((rows, ld), np.uint16)
+        full[:, :k] = bits2d
+        x = to_dev_bf16(full)[:, :k]
+    sc = to_dev_f32([s2])
+    packed, codes = nq.quantize_dynamic(x, sc)
+    p_ref, c_ref = N.quantize_dynamic(bits2d, s2)
+    assert np.array_equal(host(codes), c_ref)
+    assert np.array_equal(host(packed), p_ref)
+    out = nq.dequant(packed, codes, sc)
+    assert np.array_equal(to_host_bits(out), N.dequant(p_ref, c_ref, s2))
+
+
+def test_quantize_config3_full(path):
+    note(f"quantize_dynamic config3 full ({path})")
+    x = datagen.config3()
+    _, s2 = N.tensor_scale(x)
+    _quant_case(x, s2)
+
+
+@pytest.mark.parametrize("rows,k,ld", [(1, 16, None), (3, 48, None), (5, 4112, None), (7, 64, 72),
+                                       (300, 272, 288), (2, 8192, None)])
+def test_quantize_ragged(rows, k, ld, path):
+    note(f"quantize_dynamic rows={rows} k={k} ld={ld} ({path})")
+    rng = np.random.default_rng(rows * 131 + k)
+    x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (rows, k)).astype(np.float32))
+    _, s2 = N.tensor_scale(x)
+    _quant_case(x, s2, ld)
+
+
+def test_quantize_edge_blocks(path):
+    note(f"quantize_dynamic edge blocks ({path})")
+    s2 = 2.0 ** -8
+    qv = np.array([6, -4, 3, 0.5, -1.5, 2, 1, 0, -6, 4, -3, 0.5, 1.5, -2, -1, 6.0])
+    rows = []
+    for code in (0x01, 0x05, 0x08, 0x40, 0x7E):
+        rows.append(qv * float(F.E4M3_VALUES[code]) * s2)                      # exactly representable
+    rows.append(np.zeros(16))                                                  # zero block
+    rows.append(-np.zeros(16))                                                 # negative zeros
+    rows.append(np.full(16, 1e-30))                                            # tiny: code raised to 1
+    rows.append(np.array([5.0, 2.5, 0.75, 0.25, 1.25, 1.75, 3.5, 5.0] * 2) * float(F.E4M3_VALUES[0x38]) * s2)  # ties
+    rows.append(np.full(16, 1e6))                                              # saturating code 0x7E
+    x = datagen.f32_to_bf16_bits(np.concatenate(rows).astype(np.float32)).reshape(1, -1)
+    _quant_case(x, s2)
+    _quant_case(x, 0.0)                                                       # zero tensor scale
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_quantize_random_scales(seed, path):
+    """Odd tensor scales (not from the tensor's own amax) stress every code."""
+    note(f"quantize_dynamic random scale seed={seed} ({path})")
+    rng = np.random.default_rng(seed)
+    x = datagen.f32_to_bf16_bits((rng.standard_normal((64, 512)) * np.exp(rng.uniform(-8, 8, (64, 1)))).astype(np.float32))
+    s2 = float(np.float32(np.exp(rng.uniform(-12, 4))))
+    _quant_case(x, s2)
+
+
+def test_dequant_all_codes():
+    note("dequant all codes")
+    rng = np.random.default_rng(9)
+    rows, k = 256, 256
+    codes = rng.integers(0, 256, (rows, k // 16)).astype(np.uint8)
+    codes[0, :] = np.arange(16) + 0x70            # includes 0x7F (NaN)
+    packed = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
+    for s2 in (1.0, 3.7e-4, 2.0 ** -140):
+        out = nq.dequant(to_dev_u8(packed), to_dev_u8(codes), to_dev_f32([s2]))
+        got = to_host_bits(out)
+        ref = N.dequant(packed, codes, float(np.float32(s2)))
+        nan_g = (got & 0x7FFF) > 0x7F80
+        nan_r = (ref & 0x7FFF) > 0x7F80
+        assert np.array_equal(nan_g, nan_r)
+        assert np.array_equal(got[~nan_g], ref[~nan_r])

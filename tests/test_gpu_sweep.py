@@ -1,0 +1,137 @@
+"""GPU parity: Hessian-weighted E4M3 scale sweep against the float64 oracle.
+
+Bar (per block): the chosen code equals the oracle's on >= 99.99% of blocks;
+where it differs, the oracle's cost of the GPU's code is within 1e-5 relative
+of the oracle minimum; the nibbles always equal the oracle's quantization at
+the GPU's code, bit for bit; the fp32 cost output is within 1e-4 relative of
+the oracle's cost of that code.  H and scale_2 are the same float32 values on
+both sides (the oracle's H rounded to float32)."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import nvfp4 as N
+from oracle import formats as F
+import nvfp4_post_quantization_amd as nq
+
+from _gpu import DEV, need_gpu, note, to_dev_bf16, to_dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.fixture(params=["fast", "exact"])
+def path(request, monkeypatch):
+    if request.param == "exact":
+        monkeypatch.setenv("NVFP4MI_FORCE_EXACT", "1")
+    else:
+        monkeypatch.delenv("NVFP4MI_FORCE_EXACT", raising=False)
+    return request.param
+
+
+def gpu_sweep(w_bits, h32, s2, ld=None):
+    rows, k = w_bits.shape
+    if ld is None:
+        w = to_dev_bf16(w_bits)
+    else:
+        full = np.zeros((rows, ld), np.uint16)
+        full[:, :k] = w_bits
+        w = to_dev_bf16(full)[:, :k]
+    H = torch.from_numpy(np.ascontiguousarray(h32, dtype=np.float32)).to(DEV)
+    packed, codes, cost = nq.scale_sweep(w, H, to_dev_f32([s2]), want_cost=True)
+    return host(packed), host(codes), host(cost)
+
+
+def check_sweep(w_bits, h32, s2, ld=None, max_mismatch_frac=1e-4):
+    packed, codes, cost = gpu_sweep(w_bits, h32, s2, ld)
+    h = h32.astype(np.float64)
+    costs = N.sweep_costs(w_bits, h, s2)                        # [rows, G, 127]
+    ref = np.argmin(costs, axis=2)
+    ref_min = np.min(costs, axis=2)
+    rows, g = codes.shape
+    cg = np.take_along_axis(costs, codes.astype(np.int64)[..., None], axis=2)[..., 0]
+    w0 = costs[:, :, 0]                                         # cost of the zero scale = w^T H w
+    mism = codes != ref
+    n_mism = int(mism.sum())
+    assert n_mism <= max_mismatch_frac * codes.size, f"{n_mism} of {codes.size} codes differ"
+    if n_mism:
+        tol = np.where(ref_min > 0, 1e-5 * ref_min, 1e-5 * w0)
+        assert np.all(cg[mism] - ref_min[mism] <= tol[mism]), "a differing code is not a near-tie"
+    w = F.bf16_bits_to_f64(w_bits).reshape(rows, g, 16)
+    nib, _ = N.quantize_at_code(w, codes, s2)
+    assert np.array_equal(packed, F.pack_nibbles(nib.reshape(rows, g * 16))), "nibbles differ"
+    scale = np.maximum(cg, 1e-6 * w0)
+    assert np.all(np.abs(cost - cg) <= 1e-4 * scale + 1e-30), "cost output off"
+    return codes, n_mism
+
+
+def _inputs_c1():
+    w, x = datagen.config1()
+    h = N.hessian(x).astype(np.float32)
+    _, s2 = N.tensor_scale(w)
+    return w, h, s2
+
+
+def test_sweep_config1_full(path):
+    note(f"sweep config1 ({path})")
+    w, h, s2 = _inputs_c1()
+    check_sweep(w, h, s2)
+
+
+def test_sweep_config2_rows(path):
+    note(f"sweep config2 sampled rows ({path})")
+    w, x = datagen.config2()
+    h = N.hessian(x).astype(np.float32)
+    _, s2 = N.tensor_scale(w)                     # the tensor scale of the whole matrix
+    rows = np.sort(np.random.default_rng(2).choice(w.shape[0], 192, replace=False))
+    check_sweep(w[rows], h, s2)
+
+
+@pytest.mark.parametrize("rows,k,ld", [(1, 16, None), (5, 48, None), (13, 32, 40), (4, 2048, 2056)])
+def test_sweep_ragged(rows, k, ld, path):
+    note(f"sweep rows={rows} k={k} ld={ld} ({path})")
+    rng = np.random.default_rng(rows * 7 + k)
+    w = datagen.f32_to_bf16_bits((rng.standard_normal((rows, k)) * 0.02).astype(np.float32))
+    x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (300, k)).astype(np.float32))
+    h = N.hessian(x).astype(np.float32)
+    _, s2 = N.tensor_scale(w)
+    check_sweep(w, h, s2, ld)
+
+
+def test_sweep_special_hessians():
+    note("sweep special Hessians")
+    rng = np.random.default_rng(3)
+    w = datagen.f32_to_bf16_bits((rng.laplace(0, 0.02, (24, 64))).astype(np.float32))
+    _, s2 = N.tensor_scale(w)
+    eye = np.broadcast_to(np.eye(16, dtype=np.float32), (4, 16, 16)).copy()
+    check_sweep(w, eye, s2)
+    zero = np.zeros((4, 16, 16), np.float32)
+    codes, _ = check_sweep(w, zero, s2)
+    assert (codes == 0).all()                      # every cost is 0: lowest code wins
+    # singular H: channel 5 never active
+    x = rng.laplace(0, 1, (64, 64))
+    x[:, 5] = 0.0
+    hs = N.hessian(datagen.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float32)
+    check_sweep(w, hs, s2)
+
+
+def test_sweep_exact_and_zero_blocks(path):
+    note(f"sweep exact/zero blocks ({path})")
+    s2 = 2.0 ** -10
+    rng = np.random.default_rng(4)
+    x = datagen.f32_to_bf16_bits(rng.standard_normal((128, 32)).astype(np.float32))
+    h = N.hessian(x).astype(np.float32)
+    qv = np.array([6, -4, 3, 0.5, -1.5, 2, 1, 0, -6, 4, -3, 0.5, 1.5, -2, -1, 6.0])
+    w = np.zeros((4, 32))
+    w[0, :16] = qv * float(F.E4M3_VALUES[0x3B]) * s2
+    w[1, 16:] = qv * float(F.E4M3_VALUES[0x01]) * s2
+    w[2, :] = -0.0
+    w[3, :16] = 1e6
+    wb = datagen.f32_to_bf16_bits(w.astype(np.float32))
+    codes, _ = check_sweep(wb, h, s2)
+    assert codes[2, 0] == 0 and codes[2, 1] == 0

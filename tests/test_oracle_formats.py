@@ -84,11 +84,14 @@ def test_pack_order_low_nibble_first(page_constants):
 
 def test_e4m3_table_against_torch_and_page(page_constants):
     vals = F.E4M3_VALUES
-    assert np.isnan(vals[127])
+    assert np.isnan(vals[127]) and np.isnan(vals[255])
     assert np.nanmax(vals) == page_constants["e4m3_max"][0]
-    assert len(vals) == page_constants["e4m3_scale_codes"][0]
-    tv = torch.arange(128, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-    assert np.array_equal(vals[:127], tv[:127])
+    nonneg = vals[:128]
+    assert len(nonneg) == page_constants["e4m3_scale_codes"][0]
+    tv = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = ~np.isnan(tv)
+    assert np.array_equal(np.isnan(vals), ~fin)
+    assert np.array_equal(vals[fin], tv[fin])
     assert np.all(np.diff(vals[:127]) > 0)
 
 
