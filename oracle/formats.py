@@ -77,17 +77,19 @@ def unpack_nibbles(packed) -> np.ndarray:
 # --- E4M3FN -------------------------------------------------------------------
 
 def e4m3_value(code) -> np.ndarray:
-    """Value of non-negative E4M3FN codes 0..127 (0x7F -> NaN)."""
+    """Value of E4M3FN codes 0..255: bit 7 is the sign; 0x7F and 0xFF are NaN."""
     code = np.asarray(code).astype(np.int64)
-    e = code >> 3
-    m = code & 7
+    mag = code & 0x7F
+    e = mag >> 3
+    m = mag & 7
     sub = m * 2.0 ** -9
     nrm = (8 + m) * np.exp2(e.astype(np.float64) - 10.0)
     v = np.where(e == 0, sub, nrm)
-    return np.where(code == 0x7F, np.nan, v)
+    v = np.where(code & 0x80, -v, v)
+    return np.where(mag == 0x7F, np.nan, v)
 
 
-E4M3_VALUES = e4m3_value(np.arange(128))   # [127] is NaN
+E4M3_VALUES = e4m3_value(np.arange(256))   # [127], [255] are NaN; [128:] negative
 
 
 def e4m3_encode_ratio(num, den) -> np.ndarray:
