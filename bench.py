@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 post-training-quantization hot path on one MI355X.
+
+One step is one pass of every stage of the path over resident synthetic
+inputs:
+  * the hybrid-model MLP set (gate/up W [12288, 4096], down W [4096, 12288];
+    2^20 calibration tokens streamed as 16 chunks of 65536 per Linear input):
+      a1 tensor amax -> scale_2 of each weight,
+      a2 block-diagonal Hessian of both input streams (32 chunk calls, the
+         activation amax fused into the same read),
+      a3 the Hessian-weighted E4M3 scale sweep of all three weights
+         (9,437,184 blocks);
+  * activations X [8192, 4096]: a1 amax, a4 dynamic NVFP4 quantization and
+    a5 the dequant round trip;
+  * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast.
+
+The headline value is weight blocks swept per second of whole-step time.
+Per-stage times come from HIP events on the stream the library launches on.
+The roofline entry is the stage with the largest share of the step.  The
+cpu_baseline leg times the float64 oracle on a bounded sample of the same
+work on the host cores and extrapolates to the whole job.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, spec
+FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 matrix (and packed vector), spec
+SWEEP_FLOP_PER_BLOCK = 127 * (304 + 64)      # minimal method work per 16-element block
+C5_FALLBACK_BYTES = 32           # a fallback MX block reads and writes 16 bytes of nibbles
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU baseline leg")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a 4 GiB device copy (known bytes, for HBM counter scaling)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md for how the work would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import datagen
+    import nvfp4_post_quantization_amd as nq
+
+    lib = nq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------ inputs (untimed)
+    t0 = time.time()
+    W = {n: dev_bf16(datagen.config4_weights(n)) for n in ("gate", "up", "down")}
+    log(f"weights ready ({time.time() - t0:.1f}s)")
+    X = [[datagen.config4_chunk_torch(s, c, dev) for c in range(16)] for s in (0, 1)]
+    torch.cuda.synchronize()
+    log(f"calibration chunks ready: {sum(x.numel() for xs in X for x in xs) * 2 / 2**30:.1f} GiB ({time.time() - t0:.1f}s)")
+    x3 = dev_bf16(datagen.config3())
+    p5_host, e5_host, forced5 = datagen.config5()
+    P5 = torch.from_numpy(p5_host).to(dev)
+    E5 = torch.from_numpy(e5_host).to(dev)
+    n_forced = int(forced5.sum())
+    del p5_host, e5_host, forced5
+    log(f"all inputs resident ({time.time() - t0:.1f}s)")
+
+    # ------------------------------------------------------------ outputs / state
+    f32 = dict(dtype=torch.float32, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    H = {0: torch.zeros((256, 16, 16), **f32), 1: torch.zeros((768, 16, 16), **f32)}
+    amax_x = {0: torch.zeros(1, **f32), 1: torch.zeros(1, **f32)}
+    ws_bytes = max(nq.hessian_workspace_bytes(datagen.C4_CHUNK, k) for k in (4096, 12288))
+    ws = torch.empty(ws_bytes, **u8)
+    s2w = {n: torch.zeros(1, **f32) for n in W}
+    amw = {n: torch.zeros(1, **f32) for n in W}
+    sw_out = {n: (torch.empty((w.shape[0], w.shape[1] // 2), **u8),
+                  torch.empty((w.shape[0], w.shape[1] // 16), **u8)) for n, w in W.items()}
+    s2x3, amx3 = torch.zeros(1, **f32), torch.zeros(1, **f32)
+    q3 = (torch.empty((8192, 2048), **u8), torch.empty((8192, 256), **u8))
+    dq3 = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
+    c5 = (torch.empty((128, 2, 2048, 448), **u8), torch.empty(128, **f32), torch.empty(128, dtype=torch.int64, device=dev))
+
+    def chk(name, st):
+        if st != 0:
+            raise RuntimeError(f"{name}: {lib.nvfp4_status_string(st).decode()}")
+
+    stages = ["a1_scale2", "a2_hessian", "a3_sweep", "a4_quantize", "a5_dequant", "a6_cast"]
+    hin = {"gate": 0, "up": 0, "down": 1}
+
+    def step(ev):
+        ev["start"].record(stream)
+        for n, w in W.items():
+            chk("scale2", lib.nvfp4_compute_scale2(w.data_ptr(), w.numel(), s2w[n].data_ptr(), amw[n].data_ptr(), sptr))
+        chk("scale2", lib.nvfp4_compute_scale2(x3.data_ptr(), x3.numel(), s2x3.data_ptr(), amx3.data_ptr(), sptr))
+        ev["a1_scale2"].record(stream)
+        for s in (0, 1):
+            H[s].zero_()
+            amax_x[s].zero_()
+        for s in (0, 1):
+            for x in X[s]:
+                chk("hessian", lib.nvfp4_hessian_accum(x.data_ptr(), x.shape[0], x.shape[1], x.shape[1],
+                                                       H[s].data_ptr(), amax_x[s].data_ptr(), ws.data_ptr(),
+                                                       ws.numel(), sptr))
+        ev["a2_hessian"].record(stream)
+        for n, w in W.items():
+            p, c = sw_out[n]
+            chk("sweep", lib.nvfp4_scale_sweep(w.data_ptr(), w.shape[0], w.shape[1], w.shape[1],
+                                               H[hin[n]].data_ptr(), s2w[n].data_ptr(), p.data_ptr(),
+                                               c.data_ptr(), None, sptr))
+        ev["a3_sweep"].record(stream)
+        chk("quantize", lib.nvfp4_quantize_dynamic(x3.data_ptr(), 8192, 4096, 4096, s2x3.data_ptr(),
+                                                   q3[0].data_ptr(), q3[1].data_ptr(), sptr))
+        ev["a4_quantize"].record(stream)
+        chk("dequant", lib.nvfp4_dequant(q3[0].data_ptr(), q3[1].data_ptr(), s2x3.data_ptr(), 8192, 4096,
+                                         dq3.data_ptr(), sptr))
+        ev["a5_dequant"].record(stream)
+        chk("cast", lib.mxfp4_to_nvfp4_cast(P5.data_ptr(), E5.data_ptr(), 128, 2, 2048, 7168, c5[0].data_ptr(),
+                                            c5[1].data_ptr(), c5[2].data_ptr(), sptr))
+        ev["a6_cast"].record(stream)
+
+    def new_events():
+        return {k: torch.cuda.Event(enable_timing=True) for k in ["start"] + stages}
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+    fb = int(c5[2].sum().item())
+
+    evs = [new_events() for _ in range(args.steps)]
+    log(f"timing {args.steps} step(s)")
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_begin
+
+    # per-stage times (ms per step, averaged over the timed steps)
+    st_ms = {k: 0.0 for k in stages}
+    step_ms = 0.0
+    for ev in evs:
+        prev = ev["start"]
+        for k in stages:
+            st_ms[k] += prev.elapsed_time(ev[k]) / args.steps
+            prev = ev[k]
+        step_ms += ev["start"].elapsed_time(ev["a6_cast"]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    # algorithmic work per step
+    blocks = sum(w.numel() // 16 for w in W.values())
+    x_bytes = sum(x.numel() * 2 for xs in X for x in xs)
+    a1_bytes = sum(w.numel() * 2 for w in W.values()) + x3.numel() * 2
+    q_bytes = x3.numel() * 2.5625
+    cast_bytes = E5.numel() + c5[0].numel() + fb * C5_FALLBACK_BYTES
+    flops = blocks * SWEEP_FLOP_PER_BLOCK
+    info = {
+        "a1_scale2": dict(launches=4, bytes=a1_bytes),
+        "a2_hessian": dict(launches=32, bytes=x_bytes),
+        "a3_sweep": dict(launches=3, flops=flops, blocks=blocks),
+        "a4_quantize": dict(launches=1, bytes=q_bytes),
+        "a5_dequant": dict(launches=1, bytes=q_bytes),
+        "a6_cast": dict(launches=1, bytes=cast_bytes),
+    }
+    stage_rep = {}
+    for k in stages:
+        t = st_ms[k] / 1e3
+        d = {"ms_per_step": round(st_ms[k], 4), "launches_per_step": info[k]["launches"],
+             "share": round(st_ms[k] / step_ms, 4)}
+        if "bytes" in info[k]:
+            gbs = info[k]["bytes"] / t / 1e9
+            d.update(algorithmic_GB=round(info[k]["bytes"] / 1e9, 4), GBps=round(gbs, 1),
+                     frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        else:
+            tf = info[k]["flops"] / t / 1e12
+            d.update(blocks=info[k]["blocks"], blocks_per_s=round(info[k]["blocks"] / t, 1),
+                     TFLOPs=round(tf, 2), frac_fp32_peak=round(tf / FP32_PEAK_TFLOPS, 4))
+        stage_rep[k] = d
+    stage_rep["a6_cast"]["fallback_mx_blocks"] = fb
+    stage_rep["a6_cast"]["forced_by_generator"] = n_forced
+
+    dom = max(("a2_hessian", "a3_sweep"), key=lambda k: st_ms[k])
+    if dom == "a3_sweep":
+        per_launch_s = st_ms[dom] / 1e3 / 3
+        achieved = flops / 3 / per_launch_s / 1e12
+        roof = {"kernel": "sweep_kernel", "bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
+                "per_launch": f"{blocks // 3} blocks x {SWEEP_FLOP_PER_BLOCK} flop, {per_launch_s * 1e3:.4f} ms avg"}
+    else:
+        per_launch_s = st_ms[dom] / 1e3 / 32
+        achieved = x_bytes / 32 / per_launch_s / 1e9
+        roof = {"kernel": "hessian_partial_kernel+hessian_reduce_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "per_launch": f"{x_bytes / 32 / 1e9:.4f} GB avg, {per_launch_s * 1e3:.4f} ms avg"}
+    roof["traffic"] = traffic_from_profiles(roof["kernel"])
+
+    if args.copy_probe:
+        a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.copy_(a)
+        e0.record(stream)
+        for _ in range(5):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        stage_rep["hbm_copy_probe"] = {"bytes_read": a.numel() * 2, "bytes_written": a.numel() * 2,
+                                       "GBps": round(2 * a.numel() * 2 / (ms / 1e3) / 1e9, 1)}
+        del a, b
+
+    value = blocks / (ms_per_step / 1e3)
+    out = {
+        "metric": "weight blocks/sec (Hessian scale sweep) + accumulate/quant GB/s vs HBM peak",
+        "value": round(value, 1),
+        "unit": "weight blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "hybrid-model MLP set calibration (gate/up [12288,4096], down [4096,12288], "
+                        "2^20 tokens in 16 x 65536-token chunks: scale_2, Hessian, sweep) + activation "
+                        "quantize/dequant [8192,4096] + MXFP4->NVFP4 cast of 128 experts x (w1,w3) [2048,7168]",
+            "weight_blocks_per_step": blocks,
+            "calibration_tokens": datagen.C4_TOKENS,
+            "chunk_tokens": datagen.C4_CHUNK,
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "cpu_baseline": None,
+        "stages": stage_rep,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, X, H, s2w, blocks)
+    print(json.dumps(out), flush=True)
+
+
+def traffic_from_profiles(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    src = {"sweep_kernel": "sweep.hip"}.get(kernel.split("+")[0], "hessian.hip")
+    try:
+        sha = hashlib.sha256(open(os.path.join(ROOT, "nvfp4_post_quantization_amd", "csrc", src), "rb").read()).hexdigest()[:16]
+        for line in open(path):
+            f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+            if f.get("kernel") == kernel.split("+")[0] and f.get("src_sha") == sha:
+                return float(f["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(W, X, H, s2w, blocks):
+    """Time the float64 oracle on a bounded sample of the same job and
+    extrapolate to the whole step (Hessian of both streams + all sweeps)."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    t_tok = 32768
+    t0 = time.perf_counter()
+    hs = {}
+    for s in (0, 1):
+        xs = X[s][0][:t_tok].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        a = time.perf_counter()
+        hs[s] = oracle.hessian(xs)
+        hs[s] = time.perf_counter() - a
+    rows = {"gate": 96, "down": 32}
+    sweep_t, sweep_blocks = 0.0, 0
+    for n, r in rows.items():
+        wb = W[n][:r].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        h = H[0 if n != "down" else 1].cpu().numpy().astype(np.float64)
+        s2 = float(s2w[n].cpu().numpy()[0])
+        a = time.perf_counter()
+        oracle.scale_sweep(wb, h, s2)
+        sweep_t += time.perf_counter() - a
+        sweep_blocks += wb.size // 16
+    wall = time.perf_counter() - t0
+    full_tokens = 1 << 20
+    t_hess = (hs[0] + hs[1]) * (full_tokens / t_tok)
+    t_sweep = sweep_t / sweep_blocks * blocks
+    est = t_hess + t_sweep
+    return {
+        "value": round(blocks / est, 1),
+        "unit": "weight blocks/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle on {t_tok} tokens of each calibration stream (Hessian) and "
+                   f"{rows['gate']} gate rows + {rows['down']} down rows ({sweep_blocks} blocks, sweep), "
+                   f"extrapolated to 2^20 tokens and {blocks} blocks: est. {est:.0f} s per step "
+                   f"(Hessian {t_hess:.0f} s, sweep {t_sweep:.0f} s); sample wall {wall:.1f} s; "
+                   f"host cores visible {len(os.sched_getaffinity(0))}"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,7 @@ import numpy as np
 __all__ = [
     "stream", "f32_to_bf16_bits", "normal_bf16", "laplace_bf16",
     "config1", "config2", "config3", "config4_weights", "config4_chunk_host",
-    "config4_outlier_channels", "config5", "torch_stream_seed",
+    "config4_outlier_channels", "config4_chunk_torch", "config5", "torch_stream_seed",
     "C4_TOKENS", "C4_CHUNK", "C4_HIDDEN", "C4_INTER",
 ]
 
@@ -151,8 +151,8 @@ def config5(seed: int = 0, experts: int = 128, rows: int = 2048, k: int = 7168,
     Packed E2M1 nibbles are uniform over all 16 codes (two per byte).  Each
     32-element block has an E8M0 exponent k ~ round(N(-6, 3)); per expert the
     pair maximum k_max is taken, k is clipped to [k_max-17, k_max], and a seeded
-    ``forced_frac`` of blocks is pushed to k_max-17-U{1..4} so that the window
-    test fails for them.  Returns (packed u8 [E,2,rows,k/2], e8m0 u8
+    ``forced_frac`` of the blocks below k_max is pushed to k_max-17-U{1..4} so
+    that the window test fails for exactly those blocks.  Returns (packed u8 [E,2,rows,k/2], e8m0 u8
     [E,2,rows,k/32], forced bool [E,2,rows,k/32]).
     """
     nb = k // 32
@@ -164,8 +164,31 @@ def config5(seed: int = 0, experts: int = 128, rows: int = 2048, k: int = 7168,
     kk = np.maximum(kk, (kmax - 17)[:, None, None, None])
     rng_f = stream(5, 2, seed=seed)
     forced = rng_f.random((experts, 2, rows, nb)) < forced_frac
+    # never force a block that holds its pair's k_max (that would move k_max)
+    forced &= kk < kmax[:, None, None, None]
     drop = rng_f.integers(1, 5, size=(experts, 2, rows, nb))
     kk = np.where(forced, (kmax - 17)[:, None, None, None] - drop, kk)
     # keep every exponent inside the E8M0 finite range
     e8 = np.clip(kk + 127, 0, 254).astype(np.uint8)
     return packed, e8, forced
+
+
+def config4_chunk_torch(stream_id: int, chunk: int, device, seed: int = 0, tokens: int = C4_CHUNK):
+    """One calibration chunk drawn on the device (torch Philox, float64 draw).
+
+    Same recipe as :func:`config4_chunk_host` (Laplace(1) by the inverse CDF,
+    the same 8 outlier channels x40, float32 then bf16 rounding), but a
+    different random stream: the device draw is what the benchmark and the
+    full-size GPU checks use, and the oracle reads those very tensors back.
+    """
+    import torch
+    k = C4_HIDDEN if stream_id == 0 else C4_INTER
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_stream_seed(4, 20 + stream_id, chunk, seed))
+    u = torch.rand((tokens, k), generator=g, device=device, dtype=torch.float64)
+    u.sub_(0.5).clamp_(min=-0.5 + 2.0 ** -52)
+    x = torch.sign(u).mul_(torch.log1p(u.abs().mul_(-2.0))).neg_()
+    del u
+    ch = torch.as_tensor(config4_outlier_channels(stream_id, seed), device=device)
+    x[:, ch] *= 40.0
+    return x.to(torch.float32).to(torch.bfloat16)

@@ -17,7 +17,8 @@ void set_hip_error(hipError_t e, const char* where) {
 
 int force_exact_flag() {
   const char* v = getenv("NVFP4MI_FORCE_EXACT");
-  return (v && v[0] && v[0] != '0') ? 1 : 0;
+  if (!v || !v[0] || v[0] == '0') return 0;
+  return v[0] == '2' ? 2 : 1;
 }
 
 // a * b <= INT64_MAX for non-negative a, b

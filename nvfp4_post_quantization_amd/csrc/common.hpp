@@ -23,8 +23,9 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// NVFP4MI_FORCE_EXACT=1 in the environment disables the certified FP4-convert
-// fast path so that tests can exercise the exact threshold path everywhere.
+// Test hook read from the environment: NVFP4MI_FORCE_EXACT=1 disables the
+// certified FP4-convert fast paths (exact thresholds everywhere); =2 disables
+// only the one-float reciprocal path (two-float path where certified).
 int force_exact_flag();
 
 // Workgroups that keep every CU busy for streaming kernels (8 per CU).

@@ -11,15 +11,24 @@
 // |x| > m_k d for midpoints whose upper neighbour has an odd index and
 // |x| >= m_k d otherwise (round to nearest, ties to even), saturating at 6.
 //
-// The fast path computes y = x * r with r ~ 1/d in fp32 and lets the gfx950
+// Level 0 (fast path): y = x * r with a per-code fp32 r ~ 1/d, and the gfx950
 // FP4 convert (v_cvt_scalef32_pk_fp4_f32 with a unit scale: round to nearest
-// even, saturating, sign of zero kept) pick the code.  y is monotone in x, so
+// even, saturating, sign of zero kept) picks the code.  y is monotone in x, so
 // for a given d the fast path agrees with the exact rule for EVERY bf16 input
 // iff it agrees on the two bf16 values adjacent to each exact boundary m_k d.
-// cert_code() checks exactly those 14 inputs once per code and table build;
-// codes that fail (rare) use the exact threshold path tau_k, which compares
-// |x| against precomputed fp32 "strict" thresholds equivalent to the exact
-// comparison for every fp32 x.
+// cert_code() checks exactly those 14 inputs when the tables are built, for
+// r = RN(1/d) and its neighbours up to 4 ulps away, and keeps the first r
+// that passes.  (2688 = 2^7 * 3 * 7, so for many tensor scales some m_k d
+// fall within one fp32 rounding of a bf16 value; a shifted r usually still
+// separates them.)
+// Level 1: the quotient from a two-float reciprocal (error < 0.5 ulp + 2^-46),
+// moved one ulp toward the exact value (sign of x - y d from an fma, exact):
+// an fp32 y within one ulp of x/d can only sit on a midpoint when it is
+// there exactly, so the convert then sees the correct side of every
+// midpoint and exact ties keep the convert's ties-to-even.  Certified too.
+// Level 2 (never seen in practice): compare |x| with precomputed fp32
+// "strict" thresholds tau_k equivalent to the exact comparison for every
+// fp32 x.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -59,9 +68,21 @@ __device__ __forceinline__ void fp4x2_to_f32(uint32_t src, float& a, float& b) {
   a = v.x; b = v.y;
 }
 
-// Fast-path magnitude index of one value (used for certification only).
-__device__ __forceinline__ int fast_index(float x, float r) {
-  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x * r, 0.0f, 1.0f, 0);
+// Level-1 quotient: x / d from the two-float reciprocal (rh + rl ~ 1/d),
+// moved one ulp toward the exact quotient when it is not exact.
+__device__ __forceinline__ float quot1(float x, float d, float rh, float rl) {
+  const float y = __builtin_fmaf(x, rh, x * rl);
+  const float rho = __builtin_fmaf(-y, d, x);            // x - y*d, sign exact
+  const int dir = (rho > 0.0f) - (rho < 0.0f);
+  uint32_t b = __float_as_uint(y);
+  b += (b >> 31) ? (uint32_t)(-dir) : (uint32_t)dir;     // toward the exact value
+  return __uint_as_float(b);
+}
+
+// Magnitude index of one value on level 0 (two = false) or level 1.
+__device__ __forceinline__ int fast_index(float x, float d, float rh, float rl, bool two) {
+  float y = two ? quot1(x, d, rh, rl) : x * rh;
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, 0.0f, 1.0f, 0);
   return (int)(w & 7u);
 }
 
@@ -79,9 +100,12 @@ __device__ __forceinline__ double bf16_pattern_value(uint32_t p) {
 // Per-code constants of one tensor scale, built once per workgroup.
 struct CodeTables {
   float d[128];          // RN_f32(e4m3(c) * scale_2); d[127] = 0
-  float r[128];          // fast-path reciprocal (0 for d == 0)
-  float tau[128][8];     // exact strict thresholds for the slow path
-  uint32_t cert[4];      // bit c set: fast path exact for code c
+  float r[128];          // level-0 reciprocal (0 for d == 0)
+  float rh[128];         // two-float reciprocal, high part (level 1)
+  float rl[128];         // two-float reciprocal, low part (level 1)
+  float tau[128][8];     // exact strict thresholds for the last-resort path
+  uint32_t cert[4];      // bit c set: level 0 exact for code c
+  uint32_t cert2[4];     // bit c set: level 1 exact for code c
 };
 
 // Strict fp32 threshold tau with (|x| > tau) == (|x| passes m*d) for all fp32 x.
@@ -95,8 +119,8 @@ __device__ __forceinline__ float strict_threshold(float m, float d, bool tie_up)
   return rd;
 }
 
-// Does the fast path reproduce the exact rule for every bf16 input at (d, r)?
-__device__ __forceinline__ bool cert_code(float d, float r) {
+// Does the fast path reproduce the exact rule for every bf16 input at d?
+__device__ __forceinline__ bool cert_code(float d, float r, float rl, bool two) {
   if (d == 0.0f) return true;                  // r = 0: every code has magnitude 0
   if (!(r < 3.0e38f)) return false;
   for (int k = 0; k < 7; ++k) {
@@ -105,41 +129,65 @@ __device__ __forceinline__ bool cert_code(float d, float r) {
     bool at = bf16_pattern_value(b0) == B;
     uint32_t xp = (at && e2m1_tie_up(k)) ? b0 : b0 + 1u;   // smallest bf16 passing m_k
     if (xp <= 0x7F7Fu) {
-      if (fast_index(__uint_as_float(xp << 16), r) < k + 1) return false;
+      if (fast_index(__uint_as_float(xp << 16), d, r, rl, two) < k + 1) return false;
     }
     if (xp >= 1u) {
       uint32_t xm = xp - 1u;
       if (xm > 0x7F7Fu) xm = 0x7F7Fu;
-      if (fast_index(__uint_as_float(xm << 16), r) > k) return false;
+      if (fast_index(__uint_as_float(xm << 16), d, r, rl, two) > k) return false;
     }
   }
   return true;
 }
 
 // Fill the tables for scale_2 = s2 (call with all threads; syncs inside).
-// force_exact != 0 marks every code uncertified (exact path only; a test hook).
+// Test hook: force_exact = 1 marks every code uncertified (exact thresholds
+// only); force_exact = 2 skips only the one-float path.
 __device__ inline void build_code_tables(CodeTables& t, float s2, int force_exact) {
   int c = threadIdx.x;
-  if (c < 4) t.cert[c] = 0u;
+  if (c < 4) { t.cert[c] = 0u; t.cert2[c] = 0u; }
   __syncthreads();
   if (c < 128) {
-    float d = 0.0f, r = 0.0f;
+    float d = 0.0f, rh = 0.0f, rl = 0.0f;
     if (c < kCodes) {
       d = (float)((double)e4m3_value(c) * (double)s2);
-      r = (d == 0.0f) ? 0.0f : 1.0f / d;
+      if (d != 0.0f) {
+        double R = 1.0 / (double)d;
+        rh = (float)R;
+        rl = (float)(R - (double)rh);
+      }
     }
     t.d[c] = d;
-    t.r[c] = r;
+    t.rh[c] = rh;
+    t.rl[c] = rl;
     for (int k = 0; k < 7; ++k) t.tau[c][k] = (d == 0.0f) ? __builtin_inff() : strict_threshold(e2m1_mid(k), d, e2m1_tie_up(k));
     t.tau[c][7] = __builtin_inff();
-    bool ok = !force_exact && (c < kCodes) && cert_code(d, r);
-    if (ok) atomicOr(&t.cert[c >> 5], 1u << (c & 31));
+    float r = rh;
+    if (force_exact != 1 && c < kCodes) {
+      if (force_exact != 2) {
+        // level 0: RN(1/d), then its neighbours up to 4 ulps away
+        for (int i = 0; i < 9; ++i) {
+          const int delta = (i & 1) ? -((i + 1) >> 1) : (i >> 1);
+          const float rt = (d == 0.0f) ? 0.0f : __uint_as_float(__float_as_uint(rh) + (uint32_t)delta);
+          if (cert_code(d, rt, 0.0f, false)) {
+            r = rt;
+            atomicOr(&t.cert[c >> 5], 1u << (c & 31));
+            break;
+          }
+        }
+      }
+      if (cert_code(d, rh, rl, true)) atomicOr(&t.cert2[c >> 5], 1u << (c & 31));
+    }
+    t.r[c] = r;
   }
   __syncthreads();
 }
 
 __device__ __forceinline__ bool is_cert(const CodeTables& t, int c) {
   return (t.cert[c >> 5] >> (c & 31)) & 1u;
+}
+__device__ __forceinline__ bool is_cert2(const CodeTables& t, int c) {
+  return (t.cert2[c >> 5] >> (c & 31)) & 1u;
 }
 
 // Exact magnitude index of |x| with the code's strict thresholds.

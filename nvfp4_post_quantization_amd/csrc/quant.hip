@@ -150,6 +150,16 @@ __device__ __forceinline__ uint2 quantize_block(const uint32_t* wv, int c, const
     hi = cvt_fp4x2<2>(hi, bf16lo(wv[6]) * r, bf16hi(wv[6]) * r);
     hi = cvt_fp4x2<3>(hi, bf16lo(wv[7]) * r, bf16hi(wv[7]) * r);
     out.x = lo; out.y = hi;
+  } else if (is_cert2(t, c)) {
+    const float rh = t.rh[c], rl = t.rl[c], d = t.d[c];
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = quot1(bf16lo(wv[i]), d, rh, rl), b = quot1(bf16hi(wv[i]), d, rh, rl);
+      const uint32_t byte = cvt_fp4x2<0>(0u, a, b) & 0xFFu;
+      o[i >> 2] |= byte << (8 * (i & 3));
+    }
+    out.x = o[0]; out.y = o[1];
   } else {
     uint32_t o[2] = {0u, 0u};
     for (int e = 0; e < 16; ++e) {

@@ -23,10 +23,12 @@ def _gpu():
     need_gpu()
 
 
-@pytest.fixture(params=["fast", "exact"])
+@pytest.fixture(params=["fast", "twofloat", "exact"])
 def path(request, monkeypatch):
     if request.param == "exact":
         monkeypatch.setenv("NVFP4MI_FORCE_EXACT", "1")
+    elif request.param == "twofloat":
+        monkeypatch.setenv("NVFP4MI_FORCE_EXACT", "2")
     else:
         monkeypatch.delenv("NVFP4MI_FORCE_EXACT", raising=False)
     return request.param
@@ -134,3 +136,21 @@ def test_dequant_all_codes():
         nan_r = (ref & 0x7FFF) > 0x7F80
         assert np.array_equal(nan_g, nan_r)
         assert np.array_equal(got[~nan_g], ref[~nan_r])
+
+
+@pytest.mark.parametrize("s2", [2.0 ** -15, 2.0 ** -3, 2.0 ** -22])
+def test_quantize_short_mantissa_scale_ties(s2, path):
+    """scale_2 with a short mantissa makes every block scale short, so bf16
+    inputs hit the E2M1 midpoints exactly (the case a one-float reciprocal
+    gets wrong); every tie must go to the even neighbour."""
+    note(f"quantize_dynamic dyadic scale_2={s2} ({path})")
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rows = []
+    for code in range(1, 127):
+        d = float(F.E4M3_VALUES[code]) * s2
+        blk = np.concatenate([mids, -mids, [6.0, 0.0]]) * d      # amax 6 d: the block keeps this code
+        rows.append(blk)
+    x = datagen.f32_to_bf16_bits(np.concatenate(rows).astype(np.float32)).reshape(1, -1)
+    xv = F.bf16_bits_to_f64(x)
+    assert np.array_equal(xv[0], np.concatenate(rows)), "tie inputs must be bf16-exact"
+    _quant_case(x, s2)

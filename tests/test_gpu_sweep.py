@@ -25,10 +25,12 @@ def _gpu():
     need_gpu()
 
 
-@pytest.fixture(params=["fast", "exact"])
+@pytest.fixture(params=["fast", "twofloat", "exact"])
 def path(request, monkeypatch):
     if request.param == "exact":
         monkeypatch.setenv("NVFP4MI_FORCE_EXACT", "1")
+    elif request.param == "twofloat":
+        monkeypatch.setenv("NVFP4MI_FORCE_EXACT", "2")
     else:
         monkeypatch.delenv("NVFP4MI_FORCE_EXACT", raising=False)
     return request.param
@@ -135,3 +137,21 @@ def test_sweep_exact_and_zero_blocks(path):
     wb = datagen.f32_to_bf16_bits(w.astype(np.float32))
     codes, _ = check_sweep(wb, h, s2)
     assert codes[2, 0] == 0 and codes[2, 1] == 0
+
+
+def test_sweep_short_mantissa_scale_ties(path):
+    """A power-of-two scale_2 with blocks built on E2M1 midpoints: the sweep's
+    quantization must break every tie exactly as the oracle does."""
+    note(f"sweep dyadic scale_2 with ties ({path})")
+    s2 = 2.0 ** -15
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    rng = np.random.default_rng(8)
+    rows = []
+    for r in range(32):
+        code = int(rng.integers(8, 120))
+        d = float(F.E4M3_VALUES[code]) * s2
+        rows.append(np.concatenate([mids, -mids[::-1]]) * d * rng.choice([1.0, 2.0, 0.5], 16))
+    w = datagen.f32_to_bf16_bits(np.array(rows).astype(np.float32))
+    x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (256, 16)).astype(np.float32))
+    h = N.hessian(x).astype(np.float32)
+    check_sweep(w, h, s2)
