@@ -118,10 +118,14 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
  *          d_c = 0 quantizes to zero)
  *   cost = (w - q*d_c)^T H[g] (w - q*d_c)
  * and the code of least cost is kept (lowest code on ties).  Costs are
- * evaluated in fp32 (MFMA); the quantization itself is exact.
+ * evaluated in fp32; the quantization itself is exact.  Codes whose cost is
+ * provably larger than the best one found (Schur-complement lower bounds of
+ * H[g], with a rounding margin) are skipped, which leaves the answer
+ * unchanged.
  *
  * w       [rows][ldw] bf16, columns 0..k-1 (W of an nn.Linear: [out][in]).
- * H       [k/16][16][16] float (from nvfp4_hessian_accum).
+ * H       [k/16][16][16] float, symmetric positive semidefinite (from
+ *         nvfp4_hessian_accum); its upper triangle is read.
  * scale2  device float[1]: scale_2 of w (from nvfp4_compute_scale2).
  * packed  [rows][k/2] uint8 out: nibbles at the chosen codes.
  * codes   [rows][k/16] uint8 out: chosen E4M3 codes.

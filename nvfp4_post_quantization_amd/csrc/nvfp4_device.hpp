@@ -204,4 +204,34 @@ __device__ __forceinline__ float e2m1_mag(int idx) {
   return g[idx];
 }
 
+// Thresholds of the block-code search: code c is passed iff the block-max
+// bf16 pattern P > tp[c], where tp[c] is the largest pattern that stays at or
+// below the E4M3 midpoint between codes c and c+1 (times 6 * scale_2), ties
+// going to the even code.
+__device__ inline void build_code_search(int32_t* tp, float s2) {
+  int c = threadIdx.x;
+  if (c < 128) {
+    int32_t t = 0x7FFFFFFF;
+    if (c < kCodes - 1) {
+      double mid = 0.5 * ((double)e4m3_value(c) + (double)e4m3_value(c + 1));
+      double M = mid * 6.0 * (double)s2;                       // exact (<= 31 bits)
+      uint32_t b0 = bf16_floor_pattern(M);
+      bool at = bf16_pattern_value(b0) == M;
+      bool tie_up = ((c + 1) & 1) == 0;
+      t = (at && tie_up) ? (int32_t)b0 - 1 : (int32_t)b0;
+    }
+    tp[c] = t;
+  }
+}
+
+__device__ __forceinline__ int block_code(uint32_t P, const int32_t* tp, float s2) {
+  int pos = 0;
+#pragma unroll
+  for (int step = 64; step >= 1; step >>= 1)
+    if (tp[pos + step - 1] < (int32_t)P) pos += step;
+  if (s2 == 0.0f) pos = P ? (kCodes - 1) : 0;
+  if (pos == 0 && P) pos = 1;                                  // nonzero block: never scale 0
+  return pos;
+}
+
 }  // namespace nvfp4

@@ -3,24 +3,43 @@
 // and each finite code c, cost(c) = e^T H_g e with e = w - q(c) d_c; keep the
 // code of least cost (lowest code on ties).
 //
-// Mapping on gfx950:
-//  * a workgroup owns four adjacent groups and a range of rows; wave w sweeps
-//    group 4*blockIdx.x + w (H_g loaded once into registers) over those rows,
-//    so the four waves read each row's 128 bytes together;
-//  * the 64 lanes of a wave evaluate 16 candidate codes x 16 elements per
-//    step: lane l handles code 16*tile + l%16 and elements 4*(l/16)..+3, and
-//    eight tiles cover codes 0..127 (127 = NaN is skipped);
-//  * e = w - q d uses the certified FP4-convert fast path for q (exact for
-//    every bf16 w; uncertified codes fall back to exact thresholds);
-//  * H_g e for the 16 candidates is one 16x16x16 product, four
-//    v_mfma_f32_16x16x4_f32 with H_g as the A operand (lane l holds
-//    H_g[l%16][4*(l/16)+s]) and the error vectors as B; the output lane holds
-//    (H e)_{4*(l/16)+r} of its own candidate, so e . (H e) is a 4-term dot
-//    plus two cross-row swaps (v_permlane32/16_swap); the eight tiles' MFMA
-//    chains are independent and interleaved;
-//  * the argmin runs per lane over its 8 codes (ascending, strict <), then
-//    across the 16 candidate lanes with an explicit lowest-code tie-break.
-// Costs are fp32 (the cost output is that fp32 value); nibbles are exact.
+// Search order and exact pruning
+// ------------------------------
+// Evaluating all 127 codes per block is wasted work: far from the block's
+// max-based code the cost is provably large.  For symmetric positive
+// semidefinite H and any element i,
+//     e^T H e >= S_i e_i^2,   S_i = 1 / (H^-1)_ii   (Schur complement of H).
+// At a code c every element with |w_i| > 6 d_c saturates, and for all codes
+// c' <= c:  |e_i| >= |w_i| - 6 d_c.  At a code c every element with
+// |w_i| <= d_c / 4 quantizes to zero, and for all codes c' >= c: e_i = w_i.
+// Both bounds are monotone, so one check disposes of a whole side:
+//     LB_low(c)  = max_i S_i (|w_i| - 6 d_c)_+^2       (all codes <= c)
+//     LB_high(c) = max_{i : |w_i| <= d_c/4} S_i w_i^2   (all codes >= c)
+// Each block evaluates code 0 and its max-based code c0, then grows a window
+// [lo, hi] around c0 by one code per step, alternating sides, and closes a
+// side once its bound exceeds the best cost found by a margin (2e-5
+// relative) that covers every fp32/fp64 rounding involved, so every pruned
+// code is strictly worse than the answer.  S_i come from an fp64 Cholesky of
+// H_g and are scaled down by 1e-5; a group whose H_g is not safely positive
+// definite gets S = 0 (no pruning: every code is evaluated).
+//
+// Mapping on gfx950
+// -----------------
+//  * a workgroup = 4 waves = 4 adjacent groups; lane l of wave w handles rows
+//    r0 + l (+64, ...) of group 4*blockIdx.x + w, so the four waves read each
+//    row's 128 contiguous bytes together, and H_g is uniform per wave (its
+//    entries are scalar-register operands of the FMAs);
+//  * per step every lane evaluates one code of its own block: E2M1
+//    quantization by the certified FP4-convert paths (nvfp4_device.hpp), then
+//    the symmetric quadratic form 2 * sum_i e_i (H_ii e_i / 2 + sum_{j>i}
+//    H_ij e_j) in fp32 (152 FMA);
+//  * the wave steps until all its lanes are done (lanes that finish early
+//    idle); the nibbles are re-quantized at the chosen code.
+// fp32 MFMA and fp32 VALU share one datapath on this chip (measured: their
+// times add), so a dense MFMA product would not be cheaper than the
+// symmetric VALU form; pruning is what removes work.
+// H is taken as symmetric (its upper triangle is used), as the accumulate
+// entry point produces it.
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -30,24 +49,126 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+constexpr float kPruneMargin = 2e-5f;
 
-__device__ __forceinline__ float exact_q(float w, const float* tau) {
-  float m = e2m1_mag(exact_index(fabsf(w), tau));
-  return __builtin_copysignf(m, w);
+// sqrt(S_i) of the wave's group, S_i = (1 - 1e-5) / (H^-1)_ii with H
+// symmetrised in fp64; all zero when H is not safely positive definite.
+// Lanes 0..15 own rows 0..15 (higher lanes duplicate them).  Writes out[0..15].
+__device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
+  const int i = lane & 15;
+  double a[16];
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) a[kk] = 0.5 * ((double)Hg[i * 16 + kk] + (double)Hg[kk * 16 + i]);
+  bool ok = true;
+  double pmax = 0.0, pmin = 1e300;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const double pj = __shfl(a[j], j);              // updated A_jj from lane j
+    ok = ok && (pj > 0.0);
+    pmax = fmax(pmax, pj);
+    pmin = fmin(pmin, pj);
+    const double ljj = ok ? sqrt(pj) : 1.0;
+    const double lij = a[j] / ljj;                  // L_ij (meaningful for i >= j)
+    a[j] = lij;
+#pragma unroll
+    for (int kk = j + 1; kk < 16; ++kk) {
+      const double lkj = __shfl(lij, kk);
+      if (i >= kk) a[kk] -= lij * lkj;
+    }
+  }
+  // column i of L^-1 by forward substitution; (H^-1)_ii = sum_k y_k^2
+  double y[16];
+  double s = 0.0;
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    double acc = (kk == i) ? 1.0 : 0.0;
+#pragma unroll
+    for (int m = 0; m < kk; ++m) acc -= __shfl(a[m], kk) * y[m];
+    y[kk] = acc / __shfl(a[kk], kk);
+    s += y[kk] * y[kk];
+  }
+  ok = ok && (pmin > 1e-9 * pmax) && (s > 0.0);
+  const double S = ok ? (1.0 - 1e-5) / s : 0.0;
+  if (lane < 16) out[lane] = (float)sqrt(S);
 }
 
-__device__ __forceinline__ uint32_t exact_nib(float w, const float* tau) {
-  return (uint32_t)exact_index(fabsf(w), tau) | (__builtin_signbitf(w) ? 8u : 0u);
+// e = w - q d for the 16 elements at code c (lane-varying), exact quantization.
+__device__ __forceinline__ void block_error(const float* wv, int c, const CodeTables& t, float* e) {
+  const float d = t.d[c];
+  float q[16];
+  if (is_cert(t, c)) {
+    const float r = t.r[c];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      uint32_t nb = cvt_fp4x2<0>(0u, wv[i] * r, wv[i + 1] * r);
+      nb = cvt_fp4x2<1>(nb, wv[i + 2] * r, wv[i + 3] * r);
+      fp4x2_to_f32<0>(nb, q[i], q[i + 1]);
+      fp4x2_to_f32<1>(nb, q[i + 2], q[i + 3]);
+    }
+  } else if (is_cert2(t, c)) {
+    const float rh = t.rh[c], rl = t.rl[c];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      uint32_t nb = cvt_fp4x2<0>(0u, quot1(wv[i], d, rh, rl), quot1(wv[i + 1], d, rh, rl));
+      nb = cvt_fp4x2<1>(nb, quot1(wv[i + 2], d, rh, rl), quot1(wv[i + 3], d, rh, rl));
+      fp4x2_to_f32<0>(nb, q[i], q[i + 1]);
+      fp4x2_to_f32<1>(nb, q[i + 2], q[i + 3]);
+    }
+  } else {
+    const float* tau = t.tau[c];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = __builtin_copysignf(e2m1_mag(exact_index(fabsf(wv[i]), tau)), wv[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) e[i] = fmaf(-q[i], d, wv[i]);
 }
 
-// Sum of v over the four 16-lane rows of the wave, identical in every lane:
-// (row0 + row2) + (row1 + row3) via the gfx950 cross-row swaps.
-__device__ __forceinline__ float sum_rows(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// e^T H e with the upper triangle of H (wave-uniform):
+// 2 * sum_i e_i (hh_i e_i + sum_{j>i} H_ij e_j), hh_i = H_ii / 2.
+__device__ __forceinline__ float quad_form(const float* e, const float* __restrict__ Hg, const float* hh) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float v = hh[i] * e[i];
+#pragma unroll
+    for (int j = i + 1; j < 16; ++j) v = fmaf(Hg[i * 16 + j], e[j], v);
+    acc = fmaf(e[i], v, acc);
+  }
+  return 2.0f * acc;
+}
+
+// Nibbles of the block at code c (same quantization paths as block_error).
+__device__ __forceinline__ uint2 block_nibbles(const float* wv, int c, const CodeTables& t) {
+  uint32_t o[2] = {0u, 0u};
+  if (is_cert(t, c)) {
+    const float r = t.r[c];
+#pragma unroll
+    for (int i = 0; i < 16; i += 8) {
+      uint32_t nb = cvt_fp4x2<0>(0u, wv[i] * r, wv[i + 1] * r);
+      nb = cvt_fp4x2<1>(nb, wv[i + 2] * r, wv[i + 3] * r);
+      nb = cvt_fp4x2<2>(nb, wv[i + 4] * r, wv[i + 5] * r);
+      nb = cvt_fp4x2<3>(nb, wv[i + 6] * r, wv[i + 7] * r);
+      o[i >> 3] = nb;
+    }
+  } else if (is_cert2(t, c)) {
+    const float d = t.d[c], rh = t.rh[c], rl = t.rl[c];
+#pragma unroll
+    for (int i = 0; i < 16; i += 8) {
+      uint32_t nb = cvt_fp4x2<0>(0u, quot1(wv[i], d, rh, rl), quot1(wv[i + 1], d, rh, rl));
+      nb = cvt_fp4x2<1>(nb, quot1(wv[i + 2], d, rh, rl), quot1(wv[i + 3], d, rh, rl));
+      nb = cvt_fp4x2<2>(nb, quot1(wv[i + 4], d, rh, rl), quot1(wv[i + 5], d, rh, rl));
+      nb = cvt_fp4x2<3>(nb, quot1(wv[i + 6], d, rh, rl), quot1(wv[i + 7], d, rh, rl));
+      o[i >> 3] = nb;
+    }
+  } else {
+    const float* tau = t.tau[c];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t nib = (uint32_t)exact_index(fabsf(wv[i]), tau) | (__builtin_signbitf(wv[i]) ? 8u : 0u);
+      o[i >> 3] |= nib << ((i & 7) * 4);
+    }
+  }
+  return make_uint2(o[0], o[1]);
 }
 
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t k,
@@ -56,124 +177,115 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const uint16_t* __restr
                                                          uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
                                                          float* __restrict__ cost, int force_exact) {
   __shared__ CodeTables t;
+  __shared__ int32_t tp[128];
+  __shared__ float sqS[kWaves][16];
   const float s2 = *scale2;
-  build_code_tables(t, s2, force_exact);                     // syncs; no barrier after this point
+  build_code_search(tp, s2);
+  build_code_tables(t, s2, force_exact);                     // syncs
 
   const int64_t groups = k >> 4;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  // the four waves own four adjacent groups over the same rows, so a row's
-  // 4 x 32 bytes arrive as one 128-byte line
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-  if (g >= groups) return;
-  const int q = lane >> 4;
-  const int cl = lane & 15;
+  if (g < groups) schur_sqrt(H + g * 256, lane, sqS[wave]);
+  __syncthreads();
+  if (g >= groups) return;                                   // no barrier after this point
 
   const float* Hg = H + g * 256;
-  float hA[4];
+  float hh[16], b[16];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) hA[s] = Hg[cl * 16 + 4 * q + s];
-
-  float rt[8], dt[8];
-  uint32_t lane_cert = 0, lane_cert2 = 0, tile_slow = 0;
-#pragma unroll
-  for (int tile = 0; tile < 8; ++tile) {
-    const int c = 16 * tile + cl;
-    rt[tile] = t.r[c];
-    dt[tile] = t.d[c];
-    if (c >= kCodes || is_cert(t, c)) lane_cert |= 1u << tile;
-    if (c < kCodes && is_cert2(t, c)) lane_cert2 |= 1u << tile;
-    uint32_t bits = (t.cert[tile >> 1] >> (16 * (tile & 1))) & 0xFFFFu;
-    uint32_t need = (tile == 7) ? 0x7FFFu : 0xFFFFu;          // code 127 is not swept
-    if ((bits & need) != need) tile_slow |= 1u << tile;
+  for (int i = 0; i < 16; ++i) {
+    hh[i] = 0.5f * Hg[i * 17];
+    b[i] = sqS[wave][i];
   }
+  const float thr_scale = 1.0f + kPruneMargin;
 
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
   int64_t r1 = r0 + rows_per_wg;
   if (r1 > rows) r1 = rows;
 
-  for (int64_t r = r0; r < r1; ++r) {
-    const uint2 wv = *reinterpret_cast<const uint2*>(w + r * ldw + g * 16 + 4 * q);
-    const float w0 = bf16lo(wv.x), w1 = bf16hi(wv.x), w2 = bf16lo(wv.y), w3 = bf16hi(wv.y);
-    // error vectors of all eight tiles (lane: code 16*tile + cl, elements 4q..4q+3)
-    float e[8][4];
+  for (int64_t rb = r0; rb < r1; rb += 64) {
+    const int64_t r = rb + lane;
+    const bool valid = r < r1;
+    float wv[16];
+    {
+      const int64_t rr = valid ? r : rb;                     // rb < r1 always holds
+      const uint4* src = reinterpret_cast<const uint4*>(w + rr * ldw + g * 16);
+      const uint4 v0 = src[0], v1 = src[1];
+      const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int tile = 0; tile < 8; ++tile) {
-      const float rr = rt[tile], dd = dt[tile];
-      uint32_t nb = cvt_fp4x2<0>(0u, w0 * rr, w1 * rr);
-      nb = cvt_fp4x2<1>(nb, w2 * rr, w3 * rr);
-      float q0, q1, q2, q3;
-      fp4x2_to_f32<0>(nb, q0, q1);
-      fp4x2_to_f32<1>(nb, q2, q3);
-      if (tile_slow & (1u << tile)) {                  // wave-uniform: some code of the tile uncertified
-        if (!(lane_cert & (1u << tile))) {
-          const int c = 16 * tile + cl;
-          if (lane_cert2 & (1u << tile)) {
-            const float rh = t.rh[c], rl = t.rl[c];
-            uint32_t nb2 = cvt_fp4x2<0>(0u, quot1(w0, dd, rh, rl), quot1(w1, dd, rh, rl));
-            nb2 = cvt_fp4x2<1>(nb2, quot1(w2, dd, rh, rl), quot1(w3, dd, rh, rl));
-            fp4x2_to_f32<0>(nb2, q0, q1);
-            fp4x2_to_f32<1>(nb2, q2, q3);
+      for (int i = 0; i < 8; ++i) { wv[2 * i] = bf16lo(u[i]); wv[2 * i + 1] = bf16hi(u[i]); }
+    }
+    float a[16];
+    uint32_t P = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a[i] = b[i] * fabsf(wv[i]);
+      P = max(P, (__float_as_uint(wv[i]) >> 16) & 0x7FFFu);
+    }
+    // code 0 (zero scale): e = w
+    float best = quad_form(wv, Hg, hh);
+    int bestc = 0;
+    // nothing beats cost 0 (and code 0 is the lowest); with scale_2 = 0 every code costs w^T H w
+    bool done = !valid || best == 0.0f || s2 == 0.0f;
+    int c0 = block_code(P, tp, s2);
+    c0 = c0 < 1 ? 1 : (c0 > kCodes - 1 ? kCodes - 1 : c0);
+    {
+      float e[16];
+      block_error(wv, c0, t, e);
+      const float cc = quad_form(e, Hg, hh);
+      if (!done && cc < best) { best = cc; bestc = c0; }      // c0 > 0: a tie keeps code 0
+    }
+    int lo = c0, hi = c0, side = 0;
+    bool done_lo = false, done_hi = false;
+    while (true) {
+      int next = c0;
+      if (!done) {
+        const float thr = best * thr_scale;
+        if (!done_lo) {
+          if (lo <= 1) {
+            done_lo = true;
           } else {
-            const float* tau = t.tau[c];
-            q0 = exact_q(w0, tau); q1 = exact_q(w1, tau); q2 = exact_q(w2, tau); q3 = exact_q(w3, tau);
+            const float x = 6.0f * t.d[lo - 1];
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(-x, b[i], a[i]));
+            if (m * m > thr) done_lo = true;
           }
         }
+        if (!done_hi) {
+          if (hi >= kCodes - 1) {
+            done_hi = true;
+          } else {
+            const float qz = 0.25f * t.d[hi + 1];
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(wv[i]) <= qz ? a[i] : 0.0f);
+            if (m * m > thr) done_hi = true;
+          }
+        }
+        if (done_lo && done_hi) {
+          done = true;
+        } else {
+          const bool take_lo = !done_lo && (done_hi || side == 0);
+          next = take_lo ? lo - 1 : hi + 1;
+          side ^= 1;
+        }
       }
-      e[tile][0] = fmaf(-q0, dd, w0);
-      e[tile][1] = fmaf(-q1, dd, w1);
-      e[tile][2] = fmaf(-q2, dd, w2);
-      e[tile][3] = fmaf(-q3, dd, w3);
-    }
-    // H e for all tiles: eight independent MFMA chains, interleaved
-    floatx4 acc[8];
-#pragma unroll
-    for (int tile = 0; tile < 8; ++tile) acc[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int tile = 0; tile < 8; ++tile)
-        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x4f32(hA[s], e[tile][s], acc[tile], 0, 0, 0);
-    }
-    float best = __builtin_inff();
-    int bestc = 0;
-#pragma unroll
-    for (int tile = 0; tile < 8; ++tile) {
-      float p = e[tile][0] * acc[tile][0];
-      p = fmaf(e[tile][1], acc[tile][1], p);
-      p = fmaf(e[tile][2], acc[tile][2], p);
-      p = fmaf(e[tile][3], acc[tile][3], p);
-      p = sum_rows(p);
-      const int c = 16 * tile + cl;
-      if (c < kCodes && p < best) { best = p; bestc = c; }
-    }
-    // argmin across the 16 candidate lanes of each row (all rows agree)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int oc = __shfl_xor(bestc, o);
-      if (ob < best || (ob == best && oc < bestc)) { best = ob; bestc = oc; }
-    }
-    // nibbles of this lane's 4 elements at the chosen code
-    const float rr = t.r[bestc];
-    uint32_t nb;
-    if (is_cert(t, bestc)) {
-      nb = cvt_fp4x2<0>(0u, w0 * rr, w1 * rr);
-      nb = cvt_fp4x2<1>(nb, w2 * rr, w3 * rr);
-    } else if (is_cert2(t, bestc)) {
-      const float rh = t.rh[bestc], rl = t.rl[bestc], db = t.d[bestc];
-      nb = cvt_fp4x2<0>(0u, quot1(w0, db, rh, rl), quot1(w1, db, rh, rl));
-      nb = cvt_fp4x2<1>(nb, quot1(w2, db, rh, rl), quot1(w3, db, rh, rl));
-    } else {
-      const float* tau = t.tau[bestc];
-      nb = exact_nib(w0, tau) | (exact_nib(w1, tau) << 4) | (exact_nib(w2, tau) << 8) | (exact_nib(w3, tau) << 12);
-    }
-    if (cl == 0) {
-      *reinterpret_cast<uint16_t*>(packed + r * (k >> 1) + g * 8 + 2 * q) = (uint16_t)(nb & 0xFFFFu);
-      if (q == 0) {
-        codes[r * groups + g] = (uint8_t)bestc;
-        if (cost) cost[r * groups + g] = best;
+      if (!__any(!done)) break;                              // wave-uniform exit; at most 126 steps
+      float e[16];
+      block_error(wv, next, t, e);
+      const float cc = quad_form(e, Hg, hh);
+      if (!done) {
+        if (next < lo) lo = next; else hi = next;
+        if (cc < best || (cc == best && next < bestc)) { best = cc; bestc = next; }
       }
+    }
+    if (valid) {
+      const uint2 nb = block_nibbles(wv, bestc, t);
+      *reinterpret_cast<uint2*>(packed + r * (k >> 1) + g * 8) = nb;
+      codes[r * groups + g] = (uint8_t)bestc;
+      if (cost) cost[r * groups + g] = best;
     }
   }
 }
@@ -184,17 +296,17 @@ int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, 
                        const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s) {
   const int64_t groups = k >> 4;
   const int64_t gx = (groups + kWaves - 1) / kWaves;
-  // about 8192 workgroups; each wave sweeps rows_per_wg blocks of its group
-  int64_t rpw = (rows * gx + 8191) / 8192;
-  if (rpw < 1) rpw = 1;
+  // rows per workgroup: a multiple of 64 (one row per lane), about 4096 workgroups
+  int64_t rpw = (rows * gx + 4095) / 4096;
+  rpw = ((rpw + 63) / 64) * 64;
+  if (rpw < 64) rpw = 64;
   int64_t chunks = (rows + rpw - 1) / rpw;
   while (chunks > 65535) {
     rpw *= 2;
     chunks = (rows + rpw - 1) / rpw;
   }
   dim3 grid((unsigned)gx, (unsigned)chunks, 1);
-  sweep_kernel<<<grid, kThreads, 0, s>>>(w, rows, k, ldw, H, scale2, rpw, packed, codes, cost,
-                                                     force_exact_flag());
+  sweep_kernel<<<grid, kThreads, 0, s>>>(w, rows, k, ldw, H, scale2, rpw, packed, codes, cost, force_exact_flag());
   return launch_status("sweep_kernel");
 }
 
