@@ -198,10 +198,10 @@ __device__ __forceinline__ int exact_index(float ax, const float* tau) {
   return idx;
 }
 
-// Signed E2M1 magnitude for an index 0..7.
+// E2M1 magnitude for an index 0..7 ({0, .5, 1, 1.5, 2, 3, 4, 6}), table-free.
 __device__ __forceinline__ float e2m1_mag(int idx) {
-  const float g[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-  return g[idx];
+  const int twice = idx + max(idx - 4, 0) + 2 * max(idx - 6, 0);   // 2 * magnitude
+  return 0.5f * (float)twice;
 }
 
 // Thresholds of the block-code search: code c is passed iff the block-max

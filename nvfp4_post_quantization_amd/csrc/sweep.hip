@@ -27,14 +27,16 @@
 // -----------------
 //  * a workgroup = 4 waves = 4 adjacent groups; lane l of wave w handles rows
 //    r0 + l (+64, ...) of group 4*blockIdx.x + w, so the four waves read each
-//    row's 128 contiguous bytes together, and H_g is uniform per wave (its
-//    entries are scalar-register operands of the FMAs);
+//    row's 128 contiguous bytes together, and H_g is uniform per wave (staged
+//    in LDS and read with broadcast loads, which run beside the VALU);
 //  * per step every lane evaluates one code of its own block: E2M1
 //    quantization by the certified FP4-convert paths (nvfp4_device.hpp), then
 //    the symmetric quadratic form 2 * sum_i e_i (H_ii e_i / 2 + sum_{j>i}
-//    H_ij e_j) in fp32 (152 FMA);
+//    H_ij e_j) in fp32 (152 VALU ops);
 //  * the wave steps until all its lanes are done (lanes that finish early
 //    idle); the nibbles are re-quantized at the chosen code.
+//  * two workgroups per CU (launch bounds): the step loop fits 256 VGPRs;
+//    only the one-time table set-up spills a few values to scratch.
 // fp32 MFMA and fp32 VALU share one datapath on this chip (measured: their
 // times add), so a dense MFMA product would not be cheaper than the
 // symmetric VALU form; pruning is what removes work.
@@ -51,14 +53,14 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kPruneMargin = 2e-5f;
 
-// sqrt(S_i) of the wave's group, S_i = (1 - 1e-5) / (H^-1)_ii with H
-// symmetrised in fp64; all zero when H is not safely positive definite.
+// sqrt(S_i) of the wave's group, S_i = (1 - 1e-5) / (H^-1)_ii in fp64, H taken
+// from its upper triangle (as the cost is); all zero when H is not safely positive definite.
 // Lanes 0..15 own rows 0..15 (higher lanes duplicate them).  Writes out[0..15].
 __device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
   const int i = lane & 15;
   double a[16];
 #pragma unroll
-  for (int kk = 0; kk < 16; ++kk) a[kk] = 0.5 * ((double)Hg[i * 16 + kk] + (double)Hg[kk * 16 + i]);
+  for (int kk = 0; kk < 16; ++kk) a[kk] = (double)Hg[kk < i ? kk * 16 + i : i * 16 + kk];   // upper triangle
   bool ok = true;
   double pmax = 0.0, pmin = 1e300;
 #pragma unroll
@@ -123,9 +125,9 @@ __device__ __forceinline__ void block_error(const float* wv, int c, const CodeTa
   for (int i = 0; i < 16; ++i) e[i] = fmaf(-q[i], d, wv[i]);
 }
 
-// e^T H e with the upper triangle of H (wave-uniform):
+// e^T H e with the upper triangle of H (wave-uniform, in LDS: broadcast reads):
 // 2 * sum_i e_i (hh_i e_i + sum_{j>i} H_ij e_j), hh_i = H_ii / 2.
-__device__ __forceinline__ float quad_form(const float* e, const float* __restrict__ Hg, const float* hh) {
+__device__ __forceinline__ float quad_form(const float* e, const float* Hg, const float* hh) {
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -171,7 +173,7 @@ __device__ __forceinline__ uint2 block_nibbles(const float* wv, int c, const Cod
   return make_uint2(o[0], o[1]);
 }
 
-__global__ __launch_bounds__(kThreads) void sweep_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t k,
+__global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t k,
                                                          int64_t ldw, const float* __restrict__ H,
                                                          const float* __restrict__ scale2, int64_t rows_per_wg,
                                                          uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const uint16_t* __restr
   __shared__ CodeTables t;
   __shared__ int32_t tp[128];
   __shared__ float sqS[kWaves][16];
+  __shared__ __attribute__((aligned(16))) float Hs[kWaves][256];
   const float s2 = *scale2;
   build_code_search(tp, s2);
   build_code_tables(t, s2, force_exact);                     // syncs
@@ -187,16 +190,20 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const uint16_t* __restr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-  if (g < groups) schur_sqrt(H + g * 256, lane, sqS[wave]);
+  if (g < groups) {
+    schur_sqrt(H + g * 256, lane, sqS[wave]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Hs[wave][lane + 64 * i] = H[g * 256 + lane + 64 * i];
+  }
   __syncthreads();
   if (g >= groups) return;                                   // no barrier after this point
 
-  const float* Hg = H + g * 256;
-  float hh[16], b[16];
+  const float* Hg = Hs[wave];
+  float hh[16], b[16];                                       // wave-uniform: kept in scalar registers
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    hh[i] = 0.5f * Hg[i * 17];
-    b[i] = sqS[wave][i];
+    hh[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(0.5f * Hg[i * 17])));
+    b[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sqS[wave][i])));
   }
   const float thr_scale = 1.0f + kPruneMargin;
 
