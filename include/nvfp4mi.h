@@ -97,13 +97,15 @@ size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k);
  * and are then reduced in fp64 in a fixed order (bitwise reproducible).
  *
  * x          [tokens][ldx] bf16; columns 0..k-1 are used.
- * H          [k/16][16][16] float, in/out.
+ * H          [k/16][16][16] float, in/out, 16-byte aligned.
  * amax_inout device float[1] or NULL: if given, it is raised to
  *            max(*amax_inout, max |x|) (step 1 fused into the same read of x).
- * workspace  device buffer of at least nvfp4_hessian_workspace_bytes(tokens, k)
- *            bytes (may be NULL when that is 0); contents are scratch.
+ * workspace  16-byte aligned device buffer of at least
+ *            nvfp4_hessian_workspace_bytes(tokens, k) bytes; contents are
+ *            scratch.
  * Errors: NULL_ARG, BAD_SHAPE (tokens < 0, k <= 0, k % 16, ldx < k),
- *         MISALIGNED (x or ldx not 16-byte aligned rows), WORKSPACE, HIP.
+ *         MISALIGNED (x or ldx not 16-byte aligned rows; H or workspace not
+ *         16-byte aligned), WORKSPACE, HIP.
  */
 int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
                         float* H, float* amax_inout, void* workspace,

@@ -78,6 +78,7 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
   size_t need = hessian_workspace_bytes(tokens, k);
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (need && !workspace) return NVFP4_ERR_NULL_ARG;
+  if (!aligned16(H) || !aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
   return launch_hessian_accum(x, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
 }
 

@@ -3,9 +3,12 @@
 //
 // The work is HBM-bound (2 bytes read per element, 32 flops per element), so
 // the design goal is a single coalesced pass over X:
-//  * a workgroup owns a slab of 8 groups (128 channels, 256 B of every token
-//    row) and a contiguous token range; 64-token tiles are staged through LDS
-//    (16 B per lane, coalesced rows);
+//  * the work is cut into tiles of 64 tokens x one slab of 8 groups (128
+//    channels, 256 B of every token row).  A grid of about two workgroups per
+//    CU takes equal contiguous ranges of the slab-major tile order, so every
+//    workgroup streams the same number of bytes whatever the shape;
+//  * tiles go through LDS (16 B per lane, coalesced rows), two tiles in flight
+//    per thread;
 //  * H_g = X_g^T X_g is a 16x16 contraction over tokens, done with
 //    v_mfma_f32_16x16x32_bf16.  In that instruction lane l supplies row l%16
 //    of A and column l%16 of B for K-slots 8*(l/16)..+7; for A = X_g^T and
@@ -13,10 +16,11 @@
 //    operands.  The lane reads its 8 tokens of one channel from LDS; the
 //    16-byte chunks are XOR-swizzled by row so the four lane groups of a read
 //    hit disjoint banks;
-//  * each workgroup writes its fp32 partial H to the workspace; a second
-//    kernel adds the partials to H in fp64, in split order (deterministic).
-// Optionally the running max |x| (calibration step 1) is taken from the same
-// loads.
+//  * a workgroup writes one fp32 partial per slab its range touches (at most
+//    a few); a second kernel adds, per group, the partials of that slab's
+//    workgroups to H in fp64, in workgroup order (deterministic).
+// Optionally the running max |x| (calibration step 1) is taken from the MFMA
+// operands, which together hold every element of a tile.
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -24,134 +28,167 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kSlabGroups = 8;            // groups per workgroup
+constexpr int kSlabGroups = 8;            // groups per slab
 constexpr int kSlabCols = kSlabGroups * 16;
 constexpr int kTile = 64;                 // tokens per LDS tile
-constexpr int kRowBytes = kSlabCols * 2;  // 256
 constexpr int kThreads = 256;
-constexpr int kTargetWgs = 2048;
+constexpr int kTargetWgs = 512;           // two workgroups on each of 256 CUs (measured best)
+constexpr int kReduceParts = 4;           // workgroup sub-ranges summed in parallel by the reduce
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-struct Split {
-  int64_t slabs, splits, tiles_per_split;
+__host__ __device__ inline int64_t cdiv(int64_t n, int64_t d) { return (n + d - 1) / d; }
+
+// Work split: `total` = slabs * tiles tiles in slab-major order; workgroup w
+// owns [w*total/wgs, (w+1)*total/wgs) and writes partial slot (w, s - first
+// slab of w) for every slab s it touches (segs slots per workgroup).
+// wgs = slabs * streams with streams = kTargetWgs / slabs, so each slab's
+// token range is cut into `streams` equal parts.  Measured on MI355X: about
+// two workgroups per CU, evenly spread, streams fastest (shapes that leave
+// some CUs with a third workgroup run 15-20% slower).
+struct Plan {
+  int64_t slabs, tiles, total, wgs, segs, streams;
 };
 
-Split plan(int64_t tokens, int64_t k) {
-  Split p;
-  int64_t groups = k / 16;
-  p.slabs = (groups + kSlabGroups - 1) / kSlabGroups;
-  int64_t tiles = (tokens + kTile - 1) / kTile;
-  int64_t want = (kTargetWgs + p.slabs - 1) / p.slabs;
-  if (want < 1) want = 1;
-  if (want > tiles) want = tiles;
-  p.tiles_per_split = (tiles + want - 1) / want;
-  p.splits = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+Plan plan(int64_t tokens, int64_t k) {
+  Plan p;
+  p.slabs = cdiv(k / 16, kSlabGroups);
+  p.tiles = cdiv(tokens, kTile);
+  p.total = p.slabs * p.tiles;
+  p.streams = p.slabs < kTargetWgs ? kTargetWgs / p.slabs : 1;
+  p.wgs = p.slabs < kTargetWgs ? p.slabs * p.streams : kTargetWgs;
+  if (p.wgs > p.total) p.wgs = p.total;
+  p.segs = p.wgs > 0 ? cdiv(cdiv(p.total, p.wgs), p.tiles) + 1 : 0;
   return p;
 }
 
 // chunk position of 16-byte chunk j of tile row R
 __device__ __forceinline__ int swz(int j, int R) { return j ^ ((R >> 2) & 6); }
 
-__global__ __launch_bounds__(kThreads) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
-                                                                    int64_t k, int64_t ldx, int64_t tiles_per_split,
+__device__ __forceinline__ u16x2 abs_max2(u16x2 m, uint32_t v) {
+  return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v) & u16x2{0x7FFF, 0x7FFF});
+}
+
+__global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
+                                                                    int64_t k, int64_t ldx, int64_t tiles,
+                                                                    int64_t total, int64_t wgs, int64_t segs,
+                                                                    int64_t slabs, int64_t streams,
                                                                     float* __restrict__ ws, float* amax) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t groups = k >> 4;
-  const int64_t slab = blockIdx.x;
-  const int64_t split = blockIdx.y;
-  const int64_t col0 = slab * kSlabCols;
-  const int64_t t_begin = split * tiles_per_split * kTile;
-  int64_t t_end = t_begin + tiles_per_split * kTile;
-  if (t_end > tokens) t_end = tokens;
-  const int ntiles = (int)((t_end - t_begin + kTile - 1) / kTile);
+  // dispatch order: consecutive workgroups take neighbouring slabs of one
+  // token stream (when the grid is exactly slabs x streams)
+  const int64_t b = blockIdx.x;
+  const int64_t w = (wgs == slabs * streams) ? (b % slabs) * streams + b / slabs : b;
+  const int64_t f0 = w * total / wgs;
+  const int64_t f1 = (w + 1) * total / wgs;
+  const int64_t first_slab = f0 / tiles;
 
   // loader: thread owns chunk j = tid%16 of rows tid/16 + 16*i
   const int lj = tid & 15;
   const int lr = tid >> 4;
-  const int64_t gcol = col0 + lj * 8;
-  const bool col_ok = gcol < k;            // k % 16 == 0, so a chunk is all-in or all-out
 
   // MFMA reader: this wave owns groups 2*wave and 2*wave+1 of the slab
   const int q = lane >> 4;
   const int ch = lane & 15;
 
-  floatx4 acc[2];
-  acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
-  acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  uint32_t amx = 0;
+  u16x2 amx = u16x2{0, 0};
 
-  uint4 buf[4];
-  auto load_tile = [&](int tt) {
-    const int64_t r0 = t_begin + (int64_t)tt * kTile;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = r0 + lr + 16 * i;
-      if (col_ok && row < t_end) {
-        buf[i] = *reinterpret_cast<const uint4*>(x + row * ldx + gcol);
-      } else {
-        buf[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
+  for (int64_t f = f0; f < f1;) {
+    const int64_t slab = f / tiles;
+    const int64_t t0 = f - slab * tiles;
+    const int64_t t1 = (f1 - slab * tiles) < tiles ? (f1 - slab * tiles) : tiles;
+    const int ntiles = (int)(t1 - t0);
+    const int64_t gcol = slab * kSlabCols + lj * 8;
+    const bool col_ok = gcol < k;          // k % 16 == 0, so a chunk is all-in or all-out
 
-  if (ntiles > 0) load_tile(0);
-  for (int tt = 0; tt < ntiles; ++tt) {
-    __syncthreads();
+    floatx4 acc[2];
+    acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // two tiles in flight per thread: tile i+2 is requested as soon as tile i
+    // sits in LDS
+    uint4 bufA[4], bufB[4];
+    // per-lane part of the address; the tile's row offset is wave-uniform
+    const int64_t lane_off = (int64_t)lr * ldx + gcol;
+    auto load_tile = [&](uint4* buf, int i) {
+      const int64_t r0 = (t0 + i) * kTile;
+      const int64_t rows_left = tokens - r0;           // rows lr + 16u < rows_left exist
+      const uint16_t* base = x + r0 * ldx;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int R = lr + 16 * i;
-      *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = buf[i];
-      if (amax) {
-        uint32_t v[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          amx = max(amx, v[w] & 0x7FFFu);
-          amx = max(amx, (v[w] >> 16) & 0x7FFFu);
+      for (int u = 0; u < 4; ++u) {
+        if (col_ok && lr + 16 * u < rows_left) {
+          buf[u] = *reinterpret_cast<const uint4*>(base + lane_off + (int64_t)(16 * u) * ldx);
+        } else {
+          buf[u] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
+    };
+    auto consume = [&](uint4* buf, int i) {
+      __syncthreads();                                 // previous tile fully read
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int R = lr + 16 * u;
+        *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = buf[u];
+      }
+      __syncthreads();
+      if (i + 2 < ntiles) load_tile(buf, i + 2);
+#pragma unroll
+      for (int gsub = 0; gsub < 2; ++gsub) {
+        const int gl = 2 * wave + gsub;               // group within the slab
+        const int col = gl * 16 + ch;                 // column within the slab
+        const int j = col >> 3, within = col & 7;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          u16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int R = 32 * m + 8 * q + e;
+            v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
+          }
+          if (amax) {
+            const u32x4 d = __builtin_bit_cast(u32x4, v);
+            amx = abs_max2(abs_max2(abs_max2(abs_max2(amx, d.x), d.y), d.z), d.w);
+          }
+          const bf16x8 a = __builtin_bit_cast(bf16x8, v);
+          acc[gsub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[gsub], 0, 0, 0);
+        }
+      }
+    };
+
+    load_tile(bufA, 0);
+    if (ntiles > 1) load_tile(bufB, 1);
+    for (int i = 0; i < ntiles; i += 2) {
+      consume(bufA, i);
+      if (i + 1 < ntiles) consume(bufB, i + 1);
     }
-    __syncthreads();
-    if (tt + 1 < ntiles) load_tile(tt + 1);
+
+    // partial slot (w, slab - first_slab); lane holds C[4q + r][ch]
+    float* slot = ws + ((w * segs + (slab - first_slab)) * kSlabGroups) * 256;
 #pragma unroll
     for (int gsub = 0; gsub < 2; ++gsub) {
-      const int gl = 2 * wave + gsub;                 // group within the slab
-      const int col = gl * 16 + ch;                   // column within the slab
-      const int j = col >> 3, within = col & 7;
+      const int gl = 2 * wave + gsub;
+      if (slab * kSlabGroups + gl < groups) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        u16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int R = 32 * m + 8 * q + e;
-          v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
-        }
-        bf16x8 a = __builtin_bit_cast(bf16x8, v);
-        acc[gsub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[gsub], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) slot[gl * 256 + (4 * q + r) * 16 + ch] = acc[gsub][r];
       }
     }
+    f = slab * tiles + t1;
   }
 
-  // partial H: lane holds C[4q + r][ch]
-#pragma unroll
-  for (int gsub = 0; gsub < 2; ++gsub) {
-    const int64_t g = slab * kSlabGroups + 2 * wave + gsub;
-    if (g < groups) {
-      float* dst = ws + (split * groups + g) * 256;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(4 * q + r) * 16 + ch] = acc[gsub][r];
-    }
-  }
   if (amax) {
     __shared__ uint32_t part[kThreads / 64];
+    uint32_t am = max((uint32_t)amx.x, (uint32_t)amx.y);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, o));
-    if (lane == 0) part[wave] = amx;
+    for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+    if (lane == 0) part[wave] = am;
     __syncthreads();
     if (tid == 0) {
       uint32_t r = 0;
@@ -161,33 +198,89 @@ __global__ __launch_bounds__(kThreads) void hessian_partial_kernel(const uint16_
   }
 }
 
-// H[e] += sum over splits of ws[split][e], in fp64, split order fixed.
-__global__ __launch_bounds__(256) void hessian_reduce_kernel(const float* __restrict__ ws, int64_t splits,
-                                                              int64_t n, float* __restrict__ H) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  double s = 0.0;
-  for (int64_t p = 0; p < splits; ++p) s += (double)ws[p * n + i];
-  H[i] = (float)((double)H[i] + s);
+// H[g] += sum of the partials of group g over the workgroups whose range
+// touches g's slab, in fp64 and in workgroup order (deterministic).  One
+// workgroup per group: thread t sums float4 t%64 of the group over the t/64-th
+// of the owning workgroups; the kReduceParts sums are then added in order.
+__global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __restrict__ ws, int64_t tiles,
+                                                              int64_t total, int64_t wgs, int64_t segs,
+                                                              float4* __restrict__ H) {
+  __shared__ double part[kReduceParts][64][4];
+  const int64_t g = blockIdx.x;
+  const int64_t s = g / kSlabGroups;
+  const int gl = (int)(g % kSlabGroups);
+  const int e = threadIdx.x & 63;
+  const int c = threadIdx.x >> 6;
+  // owning workgroups of slab s: w_lo .. w_hi (all with non-empty ranges)
+  const int64_t w_lo = cdiv((s * tiles + 1) * wgs, total) - 1;
+  const int64_t w_hi = cdiv((s + 1) * tiles * wgs, total) - 1;
+  const int64_t n = w_hi - w_lo + 1;
+  const int64_t a = w_lo + n * c / kReduceParts;
+  const int64_t b = w_lo + n * (c + 1) / kReduceParts;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  auto at = [&](int64_t w) -> float4 {
+    const int64_t seg = s - (w * total / wgs) / tiles;
+    return ws[((w * segs + seg) * kSlabGroups + gl) * 64 + e];
+  };
+  int64_t w = a;
+  for (; w + 8 <= b; w += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = at(w + j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s0 += (double)v[j].x;
+      s1 += (double)v[j].y;
+      s2 += (double)v[j].z;
+      s3 += (double)v[j].w;
+    }
+  }
+  for (; w < b; ++w) {
+    const float4 v = at(w);
+    s0 += (double)v.x;
+    s1 += (double)v.y;
+    s2 += (double)v.z;
+    s3 += (double)v.w;
+  }
+  part[c][e][0] = s0;
+  part[c][e][1] = s1;
+  part[c][e][2] = s2;
+  part[c][e][3] = s3;
+  __syncthreads();
+  if (c == 0) {
+    double t[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int p = 0; p < kReduceParts; ++p) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] += part[p][e][r];
+    }
+    float4 h = H[g * 64 + e];
+    h.x = (float)((double)h.x + t[0]);
+    h.y = (float)((double)h.y + t[1]);
+    h.z = (float)((double)h.z + t[2]);
+    h.w = (float)((double)h.w + t[3]);
+    H[g * 64 + e] = h;
+  }
 }
 
 }  // namespace
 
 size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
-  Split p = plan(tokens, k);
-  return (size_t)p.splits * (size_t)(k / 16) * 256u * sizeof(float);
+  const Plan p = plan(tokens, k);
+  return (size_t)(p.wgs * p.segs) * kSlabGroups * 256u * sizeof(float);
 }
 
 int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
                          void* workspace, hipStream_t s) {
-  Split p = plan(tokens, k);
+  const Plan p = plan(tokens, k);
+  if (p.wgs == 0) return NVFP4_OK;
   float* ws = static_cast<float*>(workspace);
-  dim3 grid((unsigned)p.slabs, (unsigned)p.splits, 1);
-  hessian_partial_kernel<<<grid, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles_per_split, ws, amax);
+  hessian_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
+                                                                p.slabs, p.streams, ws, amax);
   int st = launch_status("hessian_partial_kernel");
   if (st) return st;
-  const int64_t n = (k / 16) * 256;
-  hessian_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ws, p.splits, n, H);
+  hessian_reduce_kernel<<<(unsigned)(k / 16), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles, p.total,
+                                                            p.wgs, p.segs, reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
 }
 

@@ -74,6 +74,8 @@ def test_hessian_validation(lib):
     assert f(None, 16, 32, 32, P, None, P, 1 << 20, None) == NULL
     assert f(P + 2, 16, 32, 32, P, None, P, 1 << 20, None) == ALIGN
     assert f(P, 16, 32, 36, P, None, P, 1 << 20, None) == ALIGN           # row stride not 16 B
+    assert f(P, 16, 32, 32, P + 4, None, P, 1 << 20, None) == ALIGN       # H
+    assert f(P, 16, 32, 32, P, None, P + 8, 1 << 20, None) == ALIGN       # workspace
     need = lib.nvfp4_hessian_workspace_bytes(16, 32)
     assert f(P, 16, 32, 32, P, None, P, need - 1, None) == WS
     assert f(P, 16, 32, 32, P, None, None, need, None) == NULL
