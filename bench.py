@@ -214,7 +214,7 @@ def main():
     if dom == "a3_sweep":
         per_launch_s = st_ms[dom] / 1e3 / 3
         achieved = flops / 3 / per_launch_s / 1e12
-        roof = {"kernel": "sweep_kernel", "bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
+        roof = {"kernel": "sweep_kernel", "bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
                 "per_launch": f"{blocks // 3} blocks x {SWEEP_FLOP_PER_BLOCK} flop, {per_launch_s * 1e3:.4f} ms avg"}
     else:
@@ -226,17 +226,20 @@ def main():
     roof["traffic"] = traffic_from_profiles(roof["kernel"])
 
     if args.copy_probe:
-        a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+        # an elementwise kernel of known traffic (4 GiB read + 4 GiB written per
+        # launch): the reference for scaling the HBM byte counters
+        a = torch.zeros(1 << 31, dtype=torch.int16, device=dev)
         b = torch.empty_like(a)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b.copy_(a)
+        torch.neg(a, out=b)
         e0.record(stream)
         for _ in range(5):
-            b.copy_(a)
+            torch.neg(a, out=b)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 5
-        stage_rep["hbm_copy_probe"] = {"bytes_read": a.numel() * 2, "bytes_written": a.numel() * 2,
+        stage_rep["hbm_copy_probe"] = {"kernel": "elementwise neg int16, 2^31 elements",
+                                       "bytes_read": a.numel() * 2, "bytes_written": a.numel() * 2,
                                        "GBps": round(2 * a.numel() * 2 / (ms / 1e3) / 1e9, 1)}
         del a, b
 
@@ -273,19 +276,26 @@ def main():
 
 
 def traffic_from_profiles(kernel: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source (else null)."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    probe) from the committed counter summary; null unless every kernel of
+    `kernel` ("a+b" sums them) was measured on its current source."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
-    src = {"sweep_kernel": "sweep.hip"}.get(kernel.split("+")[0], "hessian.hip")
+    srcs = {"sweep_kernel": "sweep.hip", "hessian_partial_kernel": "hessian.hip",
+            "hessian_reduce_kernel": "hessian.hip"}
+    total = 0.0
     try:
-        sha = hashlib.sha256(open(os.path.join(ROOT, "nvfp4_post_quantization_amd", "csrc", src), "rb").read()).hexdigest()[:16]
-        for line in open(path):
-            f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
-            if f.get("kernel") == kernel.split("+")[0] and f.get("src_sha") == sha:
-                return float(f["hbm_bytes_per_launch"])
+        lines = [dict(kv.split("=", 1) for kv in ln.split() if "=" in kv)
+                 for ln in open(path) if ln.startswith("kernel=")]
+        for name in kernel.split("+"):
+            src = os.path.join(ROOT, "nvfp4_post_quantization_amd", "csrc", srcs[name])
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            hit = [f for f in lines if f.get("kernel") == name and f.get("src_sha") == sha]
+            if not hit:
+                return None
+            total += float(hit[0]["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
-        pass
-    return None
+        return None
+    return round(total, 1)
 
 
 def cpu_baseline(W, X, H, s2w, blocks):

@@ -15,7 +15,7 @@ from oracle import nvfp4 as N
 from oracle import formats as F
 import nvfp4_post_quantization_amd as nq
 
-from _gpu import DEV, need_gpu, note, to_dev_bf16, to_dev_f32, host
+from _gpu import DEV, need_gpu, note, to_dev_bf16, to_dev_f32, host, compare_sweep
 
 pytestmark = pytest.mark.gpu
 
@@ -51,24 +51,7 @@ def gpu_sweep(w_bits, h32, s2, ld=None):
 
 def check_sweep(w_bits, h32, s2, ld=None, max_mismatch_frac=1e-4):
     packed, codes, cost = gpu_sweep(w_bits, h32, s2, ld)
-    h = h32.astype(np.float64)
-    costs = N.sweep_costs(w_bits, h, s2)                        # [rows, G, 127]
-    ref = np.argmin(costs, axis=2)
-    ref_min = np.min(costs, axis=2)
-    rows, g = codes.shape
-    cg = np.take_along_axis(costs, codes.astype(np.int64)[..., None], axis=2)[..., 0]
-    w0 = costs[:, :, 0]                                         # cost of the zero scale = w^T H w
-    mism = codes != ref
-    n_mism = int(mism.sum())
-    assert n_mism <= max_mismatch_frac * codes.size, f"{n_mism} of {codes.size} codes differ"
-    if n_mism:
-        tol = np.where(ref_min > 0, 1e-5 * ref_min, 1e-5 * w0)
-        assert np.all(cg[mism] - ref_min[mism] <= tol[mism]), "a differing code is not a near-tie"
-    w = F.bf16_bits_to_f64(w_bits).reshape(rows, g, 16)
-    nib, _ = N.quantize_at_code(w, codes, s2)
-    assert np.array_equal(packed, F.pack_nibbles(nib.reshape(rows, g * 16))), "nibbles differ"
-    scale = np.maximum(cg, 1e-6 * w0)
-    assert np.all(np.abs(cost - cg) <= 1e-4 * scale + 1e-30), "cost output off"
+    n_mism = compare_sweep(w_bits, h32, s2, packed, codes, cost, max_mismatch_frac)
     return codes, n_mism
 
 
