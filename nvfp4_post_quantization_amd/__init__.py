@@ -98,13 +98,20 @@ def _row_major(t: torch.Tensor, name: str) -> int:
     return t.stride(0) if t.size(0) > 1 else t.size(1)
 
 
-def compute_scale2(x: torch.Tensor):
-    """Tensor amax and scale_2 = amax / (6 * 448) of a contiguous bf16 tensor."""
+def compute_scale2(x: torch.Tensor, out=None):
+    """Tensor amax and scale_2 = amax / (6 * 448) of a contiguous bf16 tensor.
+
+    Returns (scale2, amax), each f32[1]; out=(scale2, amax) reuses buffers."""
     _dev(x, torch.bfloat16, "x")
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
-    s2 = torch.empty(1, dtype=torch.float32, device=x.device)
-    am = torch.empty(1, dtype=torch.float32, device=x.device)
+    if out is None:
+        s2 = torch.empty(1, dtype=torch.float32, device=x.device)
+        am = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        s2, am = out
+        _dev(s2, torch.float32, "scale2")
+        _dev(am, torch.float32, "amax")
     _check("nvfp4_compute_scale2",
            load().nvfp4_compute_scale2(x.data_ptr(), x.numel(), s2.data_ptr(), am.data_ptr(), _stream(x)))
     return s2, am

@@ -28,8 +28,6 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // only the one-float reciprocal path (two-float path where certified).
 int force_exact_flag();
 
-// Workgroups that keep every CU busy for streaming kernels (8 per CU).
-constexpr int kStreamGrid = 256 * 8;
 
 // Launchers (one per kernel family); arguments are validated by the caller.
 int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, hipStream_t s);

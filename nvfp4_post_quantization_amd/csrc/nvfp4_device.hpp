@@ -69,9 +69,14 @@ __device__ __forceinline__ void fp4x2_to_f32(uint32_t src, float& a, float& b) {
 }
 
 // Level-1 quotient: x / d from the two-float reciprocal (rh + rl ~ 1/d),
-// moved one ulp toward the exact quotient when it is not exact.
+// moved one ulp toward the exact quotient when it is not exact.  The low part
+// x * rl can only overflow when x * rh does too; it is then dropped, so the
+// infinite quotient keeps the sign of x (and saturates) instead of taking the
+// sign of rl.
 __device__ __forceinline__ float quot1(float x, float d, float rh, float rl) {
-  const float y = __builtin_fmaf(x, rh, x * rl);
+  float lo = x * rl;
+  lo = __builtin_isfinite(lo) ? lo : 0.0f;
+  const float y = __builtin_fmaf(x, rh, lo);
   const float rho = __builtin_fmaf(-y, d, x);            // x - y*d, sign exact
   const int dir = (rho > 0.0f) - (rho < 0.0f);
   uint32_t b = __float_as_uint(y);
@@ -103,7 +108,7 @@ struct CodeTables {
   float r[128];          // level-0 reciprocal (0 for d == 0)
   float rh[128];         // two-float reciprocal, high part (level 1)
   float rl[128];         // two-float reciprocal, low part (level 1)
-  float tau[128][8];     // exact strict thresholds for the last-resort path
+  float tau[128][8];     // exact strict thresholds (filled only for codes with neither level)
   uint32_t cert[4];      // bit c set: level 0 exact for code c
   uint32_t cert2[4];     // bit c set: level 1 exact for code c
 };
@@ -160,9 +165,8 @@ __device__ inline void build_code_tables(CodeTables& t, float s2, int force_exac
     t.d[c] = d;
     t.rh[c] = rh;
     t.rl[c] = rl;
-    for (int k = 0; k < 7; ++k) t.tau[c][k] = (d == 0.0f) ? __builtin_inff() : strict_threshold(e2m1_mid(k), d, e2m1_tie_up(k));
-    t.tau[c][7] = __builtin_inff();
     float r = rh;
+    bool level0 = false, level1 = false;
     if (force_exact != 1 && c < kCodes) {
       if (force_exact != 2) {
         // level 0: RN(1/d), then its neighbours up to 4 ulps away
@@ -171,12 +175,22 @@ __device__ inline void build_code_tables(CodeTables& t, float s2, int force_exac
           const float rt = (d == 0.0f) ? 0.0f : __uint_as_float(__float_as_uint(rh) + (uint32_t)delta);
           if (cert_code(d, rt, 0.0f, false)) {
             r = rt;
+            level0 = true;
             atomicOr(&t.cert[c >> 5], 1u << (c & 31));
             break;
           }
         }
       }
-      if (cert_code(d, rh, rl, true)) atomicOr(&t.cert2[c >> 5], 1u << (c & 31));
+      // level 1 and the exact thresholds are read only for codes that the
+      // cheaper levels do not cover, so they are built only for those
+      if (!level0 && cert_code(d, rh, rl, true)) {
+        level1 = true;
+        atomicOr(&t.cert2[c >> 5], 1u << (c & 31));
+      }
+    }
+    if (!level0 && !level1) {
+      for (int k = 0; k < 7; ++k) t.tau[c][k] = (d == 0.0f) ? __builtin_inff() : strict_threshold(e2m1_mid(k), d, e2m1_tie_up(k));
+      t.tau[c][7] = __builtin_inff();
     }
     t.r[c] = r;
   }
@@ -222,6 +236,28 @@ __device__ inline void build_code_search(int32_t* tp, float s2) {
     }
     tp[c] = t;
   }
+}
+
+// Same result as block_code, for 0 < inv = RN_f32(1 / (6 scale_2)) < inf: the
+// FP32 quotient P * inv is within 2^-23 relative of the exact one, so its E4M3
+// rounding (computed on the bits) is at most one code off, and one compare on
+// each side against the exact thresholds fixes it.
+__device__ __forceinline__ int block_code_est(uint32_t P, const int32_t* tp, float inv) {
+  const float y = __uint_as_float(P << 16) * inv;
+  int c;
+  if (y >= 0x1p-6f) {                                          // normal E4M3: 3 mantissa bits, RNE
+    const uint32_t b = __float_as_uint(y);
+    c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127 - 7) << 3);
+  } else {                                                     // subnormal E4M3: multiples of 2^-9
+    c = (int)rintf(y * 512.0f);
+  }
+  c = min(max(c, 0), kCodes - 1);
+  const int32_t hi = tp[c];
+  const int32_t lo = c > 0 ? tp[c - 1] : -1;
+  if ((int32_t)P > hi) ++c;
+  else if ((int32_t)P <= lo) --c;
+  if (c == 0 && P) c = 1;                                      // nonzero block: never scale 0
+  return c;
 }
 
 __device__ __forceinline__ int block_code(uint32_t P, const int32_t* tp, float s2) {

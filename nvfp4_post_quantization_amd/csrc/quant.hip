@@ -7,13 +7,15 @@
 // exact quotient away from FP32 rounding midpoints).
 //
 // Dynamic quantizer ("NVFP4 量化流程说明" §3.4-§3.5): one lane per 16-element
-// block.  The block code RNE(amax_b / (6 scale_2)) is found exactly by a
-// binary search over 126 bf16-pattern thresholds (one per E4M3 midpoint);
+// block.  The block code RNE(amax_b / (6 scale_2)) is estimated from the FP32
+// quotient and made exact against 126 bf16-pattern thresholds (one per E4M3
+// midpoint; binary search when 1/(6 scale_2) overflows);
 // the elements are then quantized with the certified fast path or the exact
 // threshold path (nvfp4_device.hpp).
 //
 // Dequant ("NVFP4 量化流程说明" §5.4): DQ1 d = RN_f32(e4m3 * scale_2),
-// DQ2 RN_f32(e2m1 * d), cast to BF16 (v_cvt_pk_bf16_f32, nearest even).
+// DQ2 RN_f32(e2m1 * d), cast to BF16 (v_cvt_pk_bf16_f32, nearest even); one
+// lane per half block.
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -54,25 +56,38 @@ __device__ __forceinline__ uint32_t absmax_word(uint32_t m, uint32_t v) {
   return max(m, (v >> 16) & 0x7FFFu);
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// running |x| max of two bf16 lanes at once (v_pk_max_u16 on the magnitudes)
+__device__ __forceinline__ u16x2 absmax2(u16x2 m, uint32_t v) {
+  return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v) & u16x2{0x7FFF, 0x7FFF});
+}
+
+constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per thread
+constexpr int kAmaxGrid = 512;          // two workgroups per CU (measured best for streaming)
+
 __global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                           uint32_t* acc) {
   const uint4* x16 = reinterpret_cast<const uint4*>(x);
   const int64_t n16 = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  uint32_t m = 0;
+  u16x2 m2 = u16x2{0, 0};
   int64_t i = gid;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    uint4 a = x16[i], b = x16[i + stride], c = x16[i + 2 * stride], d = x16[i + 3 * stride];
-    m = absmax_word(m, a.x); m = absmax_word(m, a.y); m = absmax_word(m, a.z); m = absmax_word(m, a.w);
-    m = absmax_word(m, b.x); m = absmax_word(m, b.y); m = absmax_word(m, b.z); m = absmax_word(m, b.w);
-    m = absmax_word(m, c.x); m = absmax_word(m, c.y); m = absmax_word(m, c.z); m = absmax_word(m, c.w);
-    m = absmax_word(m, d.x); m = absmax_word(m, d.y); m = absmax_word(m, d.z); m = absmax_word(m, d.w);
+  for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = x16[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      m2 = absmax2(m2, v[u].x); m2 = absmax2(m2, v[u].y); m2 = absmax2(m2, v[u].z); m2 = absmax2(m2, v[u].w);
+    }
   }
   for (; i < n16; i += stride) {
-    uint4 a = x16[i];
-    m = absmax_word(m, a.x); m = absmax_word(m, a.y); m = absmax_word(m, a.z); m = absmax_word(m, a.w);
+    const uint4 v = x16[i];
+    m2 = absmax2(m2, v.x); m2 = absmax2(m2, v.y); m2 = absmax2(m2, v.z); m2 = absmax2(m2, v.w);
   }
+  uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
   if (gid < n - (n16 << 3)) m = max(m, (uint32_t)x[(n16 << 3) + gid] & 0x7FFFu);
   publish_max(m, acc);
 }
@@ -93,8 +108,8 @@ int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float
   if (st) return st;
   if (n > 0) {
     int64_t n16 = n >> 3;
-    int64_t want = (n16 + 255) / 256;
-    int grid = (int)(want < kStreamGrid ? (want > 0 ? want : 1) : kStreamGrid);
+    int64_t want = (n16 + 256 * kAmaxUnroll - 1) / (256 * kAmaxUnroll);
+    int grid = (int)(want < kAmaxGrid ? (want > 0 ? want : 1) : kAmaxGrid);
     amax_reduce_kernel<<<grid, 256, 0, s>>>(x, n, acc);
     st = launch_status("amax_reduce_kernel");
     if (st) return st;
@@ -143,6 +158,20 @@ __device__ __forceinline__ uint2 quantize_block(const uint32_t* wv, int c, const
   return out;
 }
 
+constexpr int kUnits = 4;                // blocks per thread per batch (loads in flight)
+constexpr int kFlatGrid = 512;           // two workgroups per CU: each builds the code tables once
+
+// Position of flat block index u (row-major [rows][nb]) advanced by a fixed
+// stride without a 64-bit division per step.
+struct BlockPos {
+  int64_t r, g;
+  __device__ __forceinline__ void advance(int64_t dr, int64_t dg, int64_t nb) {
+    r += dr;
+    g += dg;
+    if (g >= nb) { g -= nb; ++r; }
+  }
+};
+
 __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                int64_t k, int64_t ldx,
                                                                const float* __restrict__ scale2,
@@ -150,97 +179,143 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
                                                                uint8_t* __restrict__ codes, int force_exact) {
   __shared__ CodeTables t;
   __shared__ int32_t tp[128];
+  const int64_t nb = k >> 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t dr = stride / nb, dg = stride % nb;
+  const int64_t u0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  BlockPos pos{u0 / nb, u0 % nb};
+
+  // the first batch is requested before the tables are built (it does not
+  // depend on them), so the table set-up hides under the load latency
+  uint4 v[kUnits][2];
+  auto load = [&](BlockPos p) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      if (p.r < rows) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + p.r * ldx + p.g * 16);
+        v[j][0] = src[0];
+        v[j][1] = src[1];
+      }
+      p.advance(dr, dg, nb);
+    }
+  };
+  load(pos);
   const float s2 = *scale2;
+  const float inv = (float)(1.0 / (6.0 * (double)s2));
+  const bool est = inv > 0.0f && inv < __builtin_inff();     // wave-uniform
   build_code_search(tp, s2);
   build_code_tables(t, s2, force_exact);    // syncs
-  const int64_t nb = k >> 4;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= nb) return;
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + r * ldx + g * 16);
-    uint4 v0 = src[0], v1 = src[1];
-    uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t P = 0;
+
+  while (pos.r < rows) {
+    uint32_t wv[kUnits][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) P = absmax_word(P, wv[i]);
-    int c = block_code(P, tp, s2);
-    uint2 q = quantize_block(wv, c, t);
-    *reinterpret_cast<uint2*>(packed + r * (k >> 1) + g * 8) = q;
-    codes[r * nb + g] = (uint8_t)c;
+    for (int j = 0; j < kUnits; ++j) {
+      wv[j][0] = v[j][0].x; wv[j][1] = v[j][0].y; wv[j][2] = v[j][0].z; wv[j][3] = v[j][0].w;
+      wv[j][4] = v[j][1].x; wv[j][5] = v[j][1].y; wv[j][6] = v[j][1].z; wv[j][7] = v[j][1].w;
+    }
+    BlockPos next = pos;
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) next.advance(dr, dg, nb);
+    load(next);                              // next batch in flight while this one is quantized
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      if (pos.r < rows) {
+        u16x2 m2 = u16x2{0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m2 = absmax2(m2, wv[j][i]);
+        const uint32_t P = max((uint32_t)m2.x, (uint32_t)m2.y);
+        const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
+        const uint2 q = quantize_block(wv[j], c, t);
+        *reinterpret_cast<uint2*>(packed + pos.r * (k >> 1) + pos.g * 8) = q;
+        codes[pos.r * nb + pos.g] = (uint8_t)c;
+      }
+      pos.advance(dr, dg, nb);
+    }
   }
 }
 
-static dim3 row_block_grid(int64_t rows, int64_t nb, int64_t rows_per_wg) {
-  int64_t gx = (nb + 255) / 256;
-  int64_t gy = (rows + rows_per_wg - 1) / rows_per_wg;
-  if (gy > 65535) gy = 65535;
-  if (gy < 1) gy = 1;
-  return dim3((unsigned)gx, (unsigned)gy, 1);
+static unsigned flat_grid(int64_t rows, int64_t nb) {
+  const int64_t want = (rows * nb + 256 * kUnits - 1) / (256 * kUnits);
+  return (unsigned)(want < kFlatGrid ? (want > 0 ? want : 1) : kFlatGrid);
 }
 
 int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
                             uint8_t* packed, uint8_t* codes, hipStream_t s) {
   if (rows == 0) return NVFP4_OK;
-  const int64_t nb = k >> 4;
-  // enough rows per workgroup to amortise the per-workgroup code tables
-  int64_t wgs_x = (nb + 255) / 256;
-  int64_t rpw = (rows * wgs_x + kStreamGrid - 1) / kStreamGrid;
-  if (rpw < 1) rpw = 1;
-  quantize_dynamic_kernel<<<row_block_grid(rows, nb, rpw), 256, 0, s>>>(x, rows, k, ldx, scale2, packed, codes,
-                                                                               force_exact_flag());
+  quantize_dynamic_kernel<<<flat_grid(rows, k >> 4), 256, 0, s>>>(x, rows, k, ldx, scale2, packed, codes,
+                                                                  force_exact_flag());
   return launch_status("quantize_dynamic_kernel");
 }
 
 // ---------------------------------------------------------------- dequant ----
 
+// One lane per half block (8 elements): a 4-byte nibble load and one 16-byte
+// bf16 store, so each wave instruction covers one contiguous run.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scale2, int64_t rows, int64_t k,
                                                       uint16_t* __restrict__ out) {
   __shared__ float dt[256];                 // E4M3FN: bit 7 = sign, 0x7F / 0xFF = NaN
-  const float s2 = *scale2;
+  const int64_t nh = k >> 3;                // half blocks per row
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t dr = stride / nh, dg = stride % nh;
+  const int64_t u0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  BlockPos pos{u0 / nh, u0 % nh};
+  uint32_t p[kUnits];
+  uint32_t cd[kUnits];
+  auto load = [&](BlockPos q) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      if (q.r < rows) {
+        p[j] = *reinterpret_cast<const uint32_t*>(packed + q.r * (k >> 1) + q.g * 4);
+        cd[j] = codes[q.r * (k >> 4) + (q.g >> 1)];
+      }
+      q.advance(dr, dg, nh);
+    }
+  };
+  load(pos);
   {
-    int c = threadIdx.x;
-    int m = c & 0x7F;
-    float v = m < kCodes ? (float)((double)e4m3_value(m) * (double)s2) : __builtin_nanf("");
-    dt[c] = (c & 0x80) ? -v : v;
+    const float s2 = *scale2;
+    const int c = threadIdx.x;
+    const int m = c & 0x7F;
+    const float val = m < kCodes ? (float)((double)e4m3_value(m) * (double)s2) : __builtin_nanf("");
+    dt[c] = (c & 0x80) ? -val : val;
   }
   __syncthreads();
-  const int64_t nb = k >> 4;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= nb) return;
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    const uint2 p = *reinterpret_cast<const uint2*>(packed + r * (k >> 1) + g * 8);
-    const float d = dt[codes[r * nb + g]];
-    uint32_t o[8];
+  while (pos.r < rows) {
+    uint32_t pc[kUnits], cc[kUnits];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t w = h ? p.y : p.x;
-      float a0, b0, a1, b1, a2, b2, a3, b3;
-      fp4x2_to_f32<0>(w, a0, b0);
-      fp4x2_to_f32<1>(w, a1, b1);
-      fp4x2_to_f32<2>(w, a2, b2);
-      fp4x2_to_f32<3>(w, a3, b3);
-      f32x2 v0 = {a0 * d, b0 * d}, v1 = {a1 * d, b1 * d}, v2 = {a2 * d, b2 * d}, v3 = {a3 * d, b3 * d};
-      o[4 * h + 0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2));
-      o[4 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2));
-      o[4 * h + 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2));
-      o[4 * h + 3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2));
+    for (int j = 0; j < kUnits; ++j) { pc[j] = p[j]; cc[j] = cd[j]; }
+    BlockPos next = pos;
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) next.advance(dr, dg, nh);
+    load(next);
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      if (pos.r < rows) {
+        const float d = dt[cc[j]];
+        const uint32_t w = pc[j];
+        float a0, b0, a1, b1, a2, b2, a3, b3;
+        fp4x2_to_f32<0>(w, a0, b0);
+        fp4x2_to_f32<1>(w, a1, b1);
+        fp4x2_to_f32<2>(w, a2, b2);
+        fp4x2_to_f32<3>(w, a3, b3);
+        f32x2 v0 = {a0 * d, b0 * d}, v1 = {a1 * d, b1 * d}, v2 = {a2 * d, b2 * d}, v3 = {a3 * d, b3 * d};
+        *reinterpret_cast<uint4*>(out + pos.r * k + pos.g * 8) =
+            make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2)));
+      }
+      pos.advance(dr, dg, nh);
     }
-    uint4* dst = reinterpret_cast<uint4*>(out + r * k + g * 16);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
 int launch_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2, int64_t rows, int64_t k,
                    uint16_t* out, hipStream_t s) {
   if (rows == 0) return NVFP4_OK;
-  const int64_t nb = k >> 4;
-  int64_t wgs_x = (nb + 255) / 256;
-  int64_t rpw = (rows * wgs_x + kStreamGrid - 1) / kStreamGrid;
-  if (rpw < 1) rpw = 1;
-  dequant_kernel<<<row_block_grid(rows, nb, rpw), 256, 0, s>>>(packed, codes, scale2, rows, k, out);
+  dequant_kernel<<<flat_grid(rows, k >> 3), 256, 0, s>>>(packed, codes, scale2, rows, k, out);
   return launch_status("dequant_kernel");
 }
 

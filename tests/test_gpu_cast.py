@@ -30,7 +30,8 @@ def _check(packed, e8):
 
 
 @pytest.mark.parametrize("seed,experts,rows,k,frac", [(0, 4, 64, 512, 0.01), (1, 3, 16, 7168, 0.005),
-                                                      (2, 2, 8, 256, 0.2)])
+                                                      (2, 2, 8, 256, 0.2),
+                                                      (3, 3, 96, 4096, 0.01)])   # 1.5 kmax steps per group
 def test_cast_small(seed, experts, rows, k, frac):
     note(f"cast seed={seed} experts={experts} rows={rows} k={k}")
     packed, e8, forced = datagen.config5(seed=seed, experts=experts, rows=rows, k=k, forced_frac=frac)
@@ -61,4 +62,18 @@ def test_cast_zero_halves_and_extremes():
     e8[0, 1, 2, 1] = 254                  # k_max = 127
     e8[1] = rng.integers(0, 30, (m, r, k // 32)).astype(np.uint8)   # tiny exponents
     e8[1, 0, 0, 0] = 0
+    _check(packed, e8)
+
+
+def test_cast_subnormal_tensor_scale():
+    """Groups whose largest exponent is tiny (E8M0 codes 0..8): scale_2 =
+    2^(k_max - 8) is an FP32 subnormal."""
+    note("cast subnormal scale_2")
+    rng = np.random.default_rng(6)
+    g, m, r, k = 9, 2, 4, 64
+    packed = rng.integers(0, 256, (g, m, r, k // 2)).astype(np.uint8)
+    e8 = np.zeros((g, m, r, k // 32), np.uint8)
+    for i in range(g):
+        e8[i] = rng.integers(0, i + 1, (m, r, k // 32))   # k_max code <= i
+        e8[i, 0, 0, 0] = i
     _check(packed, e8)

@@ -154,3 +154,14 @@ def test_quantize_short_mantissa_scale_ties(s2, path):
     xv = F.bf16_bits_to_f64(x)
     assert np.array_equal(xv[0], np.concatenate(rows)), "tie inputs must be bf16-exact"
     _quant_case(x, s2)
+
+
+@pytest.mark.parametrize("s2", [2.0 ** -140, 2.0 ** -128, 1e-38, 1e-30, 1e30])
+def test_quantize_extreme_scales(s2, path):
+    """Tensor scales whose 1/(6 scale_2) overflows FP32 (exact search path) or
+    whose quotients underflow (every nonzero block raised to code 0x01)."""
+    note(f"quantize_dynamic extreme scale_2={s2} ({path})")
+    rng = np.random.default_rng(11)
+    mag = np.exp(rng.uniform(np.log(1e-38), np.log(3e38), (16, 256)))
+    x = datagen.f32_to_bf16_bits((mag * rng.choice([-1.0, 1.0], (16, 256))).astype(np.float32))
+    _quant_case(x, float(np.float32(s2)))

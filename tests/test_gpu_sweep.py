@@ -138,3 +138,18 @@ def test_sweep_short_mantissa_scale_ties(path):
     x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (256, 16)).astype(np.float32))
     h = N.hessian(x).astype(np.float32)
     check_sweep(w, h, s2)
+
+
+@pytest.mark.parametrize("s2", [2.0 ** -128, 1e-30])
+def test_sweep_extreme_scales(s2, path):
+    """Tiny tensor scales with weights up to 1e12: quotients w/d overflow FP32
+    for the large codes.  Costs of most codes then agree to far below FP32
+    resolution, so codes may differ from the float64 argmin, but every
+    difference must be a near-tie and every nibble exact at the GPU's code."""
+    note(f"sweep extreme scale_2={s2} ({path})")
+    rng = np.random.default_rng(12)
+    mag = np.exp(rng.uniform(np.log(1e-38), np.log(1e12), (24, 64)))
+    w = datagen.f32_to_bf16_bits((mag * rng.choice([-1.0, 1.0], (24, 64))).astype(np.float32))
+    x = datagen.f32_to_bf16_bits(rng.standard_normal((300, 64)).astype(np.float32))
+    h = N.hessian(x).astype(np.float32)
+    check_sweep(w, h, float(np.float32(s2)), max_mismatch_frac=1.0)
