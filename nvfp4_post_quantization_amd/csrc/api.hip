@@ -18,7 +18,7 @@ void set_hip_error(hipError_t e, const char* where) {
 int force_exact_flag() {
   const char* v = getenv("NVFP4MI_FORCE_EXACT");
   if (!v || !v[0] || v[0] == '0') return 0;
-  return v[0] == '2' ? 2 : 1;
+  return (v[0] == '2' || v[0] == '3') ? v[0] - '0' : 1;
 }
 
 // a * b <= INT64_MAX for non-negative a, b

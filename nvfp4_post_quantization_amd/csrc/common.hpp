@@ -24,8 +24,9 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Test hook read from the environment: NVFP4MI_FORCE_EXACT=1 disables the
-// certified FP4-convert fast paths (exact thresholds everywhere); =2 disables
-// only the one-float reciprocal path (two-float path where certified).
+// certified FP4-convert fast paths (exact thresholds everywhere); =2 skips the
+// one-float reciprocal (level 0); =3 skips level 0 and the uncorrected
+// two-float quotient (level 1), leaving the corrected one where certified.
 int force_exact_flag();
 
 

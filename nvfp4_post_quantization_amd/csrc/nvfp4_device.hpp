@@ -84,9 +84,22 @@ __device__ __forceinline__ float quot1(float x, float d, float rh, float rl) {
   return __uint_as_float(b);
 }
 
-// Magnitude index of one value on level 0 (two = false) or level 1.
-__device__ __forceinline__ int fast_index(float x, float d, float rh, float rl, bool two) {
-  float y = two ? quot1(x, d, rh, rl) : x * rh;
+// Level-1 quotient: x / d from the two-float reciprocal, one rounding, no
+// correction (the low part is dropped when it overflows, as in quot1).
+__device__ __forceinline__ float quot_tf(float x, float rh, float rl) {
+  float lo = x * rl;
+  lo = __builtin_isfinite(lo) ? lo : 0.0f;
+  return __builtin_fmaf(x, rh, lo);
+}
+
+// Fast quotient of one level: 0 = x * r (r = rh), 1 = quot_tf, 2 = quot1.
+__device__ __forceinline__ float fast_quot(float x, float d, float rh, float rl, int level) {
+  return level == 0 ? x * rh : (level == 1 ? quot_tf(x, rh, rl) : quot1(x, d, rh, rl));
+}
+
+// Magnitude index of one value on a fast level.
+__device__ __forceinline__ int fast_index(float x, float d, float rh, float rl, int level) {
+  const float y = fast_quot(x, d, rh, rl, level);
   uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, 0.0f, 1.0f, 0);
   return (int)(w & 7u);
 }
@@ -108,9 +121,11 @@ struct CodeTables {
   float r[128];          // level-0 reciprocal (0 for d == 0)
   float rh[128];         // two-float reciprocal, high part (level 1)
   float rl[128];         // two-float reciprocal, low part (level 1)
-  float tau[128][8];     // exact strict thresholds (filled only for codes with neither level)
-  uint32_t cert[4];      // bit c set: level 0 exact for code c
-  uint32_t cert2[4];     // bit c set: level 1 exact for code c
+  float tau[128][8];     // exact strict thresholds (filled only for codes without a fast level)
+  uint32_t cert[4];      // bit c set: level 0 (x * r) exact for code c
+  uint32_t cert1[4];     // bit c set: level 1 (two-float, one rounding) exact for code c
+  uint32_t cert2[4];     // bit c set: level 2 (two-float, corrected) exact for code c
+  int mode;              // 0: level 0 for every code; 1: level 1 for every code; 2: per code
 };
 
 // Strict fp32 threshold tau with (|x| > tau) == (|x| passes m*d) for all fp32 x.
@@ -125,7 +140,7 @@ __device__ __forceinline__ float strict_threshold(float m, float d, bool tie_up)
 }
 
 // Does the fast path reproduce the exact rule for every bf16 input at d?
-__device__ __forceinline__ bool cert_code(float d, float r, float rl, bool two) {
+__device__ __forceinline__ bool cert_code(float d, float r, float rl, int level) {
   if (d == 0.0f) return true;                  // r = 0: every code has magnitude 0
   if (!(r < 3.0e38f)) return false;
   for (int k = 0; k < 7; ++k) {
@@ -134,26 +149,30 @@ __device__ __forceinline__ bool cert_code(float d, float r, float rl, bool two) 
     bool at = bf16_pattern_value(b0) == B;
     uint32_t xp = (at && e2m1_tie_up(k)) ? b0 : b0 + 1u;   // smallest bf16 passing m_k
     if (xp <= 0x7F7Fu) {
-      if (fast_index(__uint_as_float(xp << 16), d, r, rl, two) < k + 1) return false;
+      if (fast_index(__uint_as_float(xp << 16), d, r, rl, level) < k + 1) return false;
     }
     if (xp >= 1u) {
       uint32_t xm = xp - 1u;
       if (xm > 0x7F7Fu) xm = 0x7F7Fu;
-      if (fast_index(__uint_as_float(xm << 16), d, r, rl, two) > k) return false;
+      if (fast_index(__uint_as_float(xm << 16), d, r, rl, level) > k) return false;
     }
   }
   return true;
 }
 
 // Fill the tables for scale_2 = s2 (call with all threads; syncs inside).
-// Test hook: force_exact = 1 marks every code uncertified (exact thresholds
-// only); force_exact = 2 skips only the one-float path.
+// Levels are tried cheapest first; when every code is exact on one level, that
+// level serves all codes (a uniform branch in the kernels, which matters
+// since the lanes of a wave quantize at different codes).  Test hook:
+// force_exact = 1 uses the exact thresholds only, 2 skips level 0, 3 skips
+// levels 0 and 1.
 __device__ inline void build_code_tables(CodeTables& t, float s2, int force_exact) {
-  int c = threadIdx.x;
-  if (c < 4) { t.cert[c] = 0u; t.cert2[c] = 0u; }
+  const int c = threadIdx.x;
+  if (c < 4) { t.cert[c] = 0u; t.cert1[c] = 0u; t.cert2[c] = 0u; }
   __syncthreads();
+  float d = 0.0f, rh = 0.0f, rl = 0.0f;
+  bool level0 = false;
   if (c < 128) {
-    float d = 0.0f, rh = 0.0f, rl = 0.0f;
     if (c < kCodes) {
       d = (float)((double)e4m3_value(c) * (double)s2);
       if (d != 0.0f) {
@@ -166,42 +185,61 @@ __device__ inline void build_code_tables(CodeTables& t, float s2, int force_exac
     t.rh[c] = rh;
     t.rl[c] = rl;
     float r = rh;
-    bool level0 = false, level1 = false;
-    if (force_exact != 1 && c < kCodes) {
-      if (force_exact != 2) {
-        // level 0: RN(1/d), then its neighbours up to 4 ulps away
-        for (int i = 0; i < 9; ++i) {
-          const int delta = (i & 1) ? -((i + 1) >> 1) : (i >> 1);
-          const float rt = (d == 0.0f) ? 0.0f : __uint_as_float(__float_as_uint(rh) + (uint32_t)delta);
-          if (cert_code(d, rt, 0.0f, false)) {
-            r = rt;
-            level0 = true;
-            atomicOr(&t.cert[c >> 5], 1u << (c & 31));
-            break;
-          }
+    if (force_exact == 0 && c < kCodes) {
+      // level 0: RN(1/d), then its neighbours up to 4 ulps away
+      for (int i = 0; i < 9; ++i) {
+        const int delta = (i & 1) ? -((i + 1) >> 1) : (i >> 1);
+        const float rt = (d == 0.0f) ? 0.0f : __uint_as_float(__float_as_uint(rh) + (uint32_t)delta);
+        if (cert_code(d, rt, 0.0f, 0)) {
+          r = rt;
+          level0 = true;
+          atomicOr(&t.cert[c >> 5], 1u << (c & 31));
+          break;
         }
       }
-      // level 1 and the exact thresholds are read only for codes that the
-      // cheaper levels do not cover, so they are built only for those
-      if (!level0 && cert_code(d, rh, rl, true)) {
-        level1 = true;
-        atomicOr(&t.cert2[c >> 5], 1u << (c & 31));
-      }
-    }
-    if (!level0 && !level1) {
-      for (int k = 0; k < 7; ++k) t.tau[c][k] = (d == 0.0f) ? __builtin_inff() : strict_threshold(e2m1_mid(k), d, e2m1_tie_up(k));
-      t.tau[c][7] = __builtin_inff();
     }
     t.r[c] = r;
   }
   __syncthreads();
+  // codes 0..126 all on level 0: one uniform path, nothing else to build
+  const bool all0 = t.cert[0] == ~0u && t.cert[1] == ~0u && t.cert[2] == ~0u && t.cert[3] == 0x7FFFFFFFu;
+  if (all0) {
+    if (c == 0) t.mode = 0;
+    __syncthreads();
+    return;
+  }
+  // level 1 for every code, so that one uniform path may serve them all
+  bool level1 = false;
+  if (force_exact != 1 && force_exact != 3 && c < kCodes && cert_code(d, rh, rl, 1)) {
+    level1 = true;
+    atomicOr(&t.cert1[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  const bool all1 = t.cert1[0] == ~0u && t.cert1[1] == ~0u && t.cert1[2] == ~0u && t.cert1[3] == 0x7FFFFFFFu;
+  if (!all1 && c < 128) {
+    // per-code dispatch: level 2 and the exact thresholds for codes that
+    // neither cheaper level covers
+    bool level2 = false;
+    if (!level0 && !level1 && force_exact != 1 && c < kCodes && cert_code(d, rh, rl, 2)) {
+      level2 = true;
+      atomicOr(&t.cert2[c >> 5], 1u << (c & 31));
+    }
+    if (!level0 && !level1 && !level2) {
+      for (int k = 0; k < 7; ++k) t.tau[c][k] = (d == 0.0f) ? __builtin_inff() : strict_threshold(e2m1_mid(k), d, e2m1_tie_up(k));
+      t.tau[c][7] = __builtin_inff();
+    }
+  }
+  if (c == 0) t.mode = all1 ? 1 : 2;
+  __syncthreads();
 }
 
-__device__ __forceinline__ bool is_cert(const CodeTables& t, int c) {
-  return (t.cert[c >> 5] >> (c & 31)) & 1u;
-}
-__device__ __forceinline__ bool is_cert2(const CodeTables& t, int c) {
-  return (t.cert2[c >> 5] >> (c & 31)) & 1u;
+// Fast level used for code c (3 = exact thresholds); uniform unless mode == 2.
+__device__ __forceinline__ int code_level(const CodeTables& t, int c) {
+  if (t.mode != 2) return t.mode;
+  if ((t.cert[c >> 5] >> (c & 31)) & 1u) return 0;
+  if ((t.cert1[c >> 5] >> (c & 31)) & 1u) return 1;
+  if ((t.cert2[c >> 5] >> (c & 31)) & 1u) return 2;
+  return 3;
 }
 
 // Exact magnitude index of |x| with the code's strict thresholds.
@@ -211,6 +249,49 @@ __device__ __forceinline__ int exact_index(float ax, const float* tau) {
   for (int k = 0; k < 7; ++k) idx += (ax > tau[k]) ? 1 : 0;
   return idx;
 }
+
+// Packed E2M1 nibbles of 16 values at code c on one level (element 2i in the
+// low nibble of byte i): levels 0-2 through the FP4 convert (RNE, saturating)
+// of the certified fast quotient, level 3 by the exact thresholds.
+template <int LEVEL>
+__device__ __forceinline__ uint2 nibbles16_level(const float* x, int c, const CodeTables& t) {
+  uint32_t o[2] = {0u, 0u};
+  if constexpr (LEVEL == 3) {
+    const float* tau = t.tau[c];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t nib = (uint32_t)exact_index(fabsf(x[i]), tau) | (__builtin_signbitf(x[i]) ? 8u : 0u);
+      o[i >> 3] |= nib << ((i & 7) * 4);
+    }
+  } else {
+    const float d = t.d[c], rh = LEVEL == 0 ? t.r[c] : t.rh[c], rl = t.rl[c];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* v = x + 8 * h;
+      uint32_t nb = cvt_fp4x2<0>(0u, fast_quot(v[0], d, rh, rl, LEVEL), fast_quot(v[1], d, rh, rl, LEVEL));
+      nb = cvt_fp4x2<1>(nb, fast_quot(v[2], d, rh, rl, LEVEL), fast_quot(v[3], d, rh, rl, LEVEL));
+      nb = cvt_fp4x2<2>(nb, fast_quot(v[4], d, rh, rl, LEVEL), fast_quot(v[5], d, rh, rl, LEVEL));
+      nb = cvt_fp4x2<3>(nb, fast_quot(v[6], d, rh, rl, LEVEL), fast_quot(v[7], d, rh, rl, LEVEL));
+      o[h] = nb;
+    }
+  }
+  return make_uint2(o[0], o[1]);
+}
+
+// Nibbles of 16 values at code c (lane-varying).  mode = t.mode, read once
+// per kernel into a scalar register: modes 0 and 1 take one level for every
+// code (a uniform branch); mode 2 dispatches per code.
+__device__ __forceinline__ uint2 nibbles16(const float* x, int c, const CodeTables& t, int mode) {
+  if (mode == 0) return nibbles16_level<0>(x, c, t);
+  if (mode == 1) return nibbles16_level<1>(x, c, t);
+  const int lvl = code_level(t, c);
+  if (lvl == 0) return nibbles16_level<0>(x, c, t);
+  if (lvl == 1) return nibbles16_level<1>(x, c, t);
+  if (lvl == 2) return nibbles16_level<2>(x, c, t);
+  return nibbles16_level<3>(x, c, t);
+}
+
+__device__ __forceinline__ int table_mode(const CodeTables& t) { return __builtin_amdgcn_readfirstlane(t.mode); }
 
 // E2M1 magnitude for an index 0..7 ({0, .5, 1, 1.5, 2, 3, 4, 6}), table-free.
 __device__ __forceinline__ float e2m1_mag(int idx) {

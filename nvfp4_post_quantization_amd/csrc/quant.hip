@@ -121,41 +121,11 @@ int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float
 // ------------------------------------------------------ dynamic quantizer ----
 
 // Quantize 8 words (16 bf16) at code c; returns the two packed dwords.
-__device__ __forceinline__ uint2 quantize_block(const uint32_t* wv, int c, const CodeTables& t) {
-  uint2 out;
-  const float r = t.r[c];
-  if (is_cert(t, c)) {
-    uint32_t lo = 0, hi = 0;
-    lo = cvt_fp4x2<0>(lo, bf16lo(wv[0]) * r, bf16hi(wv[0]) * r);
-    lo = cvt_fp4x2<1>(lo, bf16lo(wv[1]) * r, bf16hi(wv[1]) * r);
-    lo = cvt_fp4x2<2>(lo, bf16lo(wv[2]) * r, bf16hi(wv[2]) * r);
-    lo = cvt_fp4x2<3>(lo, bf16lo(wv[3]) * r, bf16hi(wv[3]) * r);
-    hi = cvt_fp4x2<0>(hi, bf16lo(wv[4]) * r, bf16hi(wv[4]) * r);
-    hi = cvt_fp4x2<1>(hi, bf16lo(wv[5]) * r, bf16hi(wv[5]) * r);
-    hi = cvt_fp4x2<2>(hi, bf16lo(wv[6]) * r, bf16hi(wv[6]) * r);
-    hi = cvt_fp4x2<3>(hi, bf16lo(wv[7]) * r, bf16hi(wv[7]) * r);
-    out.x = lo; out.y = hi;
-  } else if (is_cert2(t, c)) {
-    const float rh = t.rh[c], rl = t.rl[c], d = t.d[c];
-    uint32_t o[2] = {0u, 0u};
+__device__ __forceinline__ uint2 quantize_block(const uint32_t* wv, int c, const CodeTables& t, int mode) {
+  float x[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a = quot1(bf16lo(wv[i]), d, rh, rl), b = quot1(bf16hi(wv[i]), d, rh, rl);
-      const uint32_t byte = cvt_fp4x2<0>(0u, a, b) & 0xFFu;
-      o[i >> 2] |= byte << (8 * (i & 3));
-    }
-    out.x = o[0]; out.y = o[1];
-  } else {
-    uint32_t o[2] = {0u, 0u};
-    for (int e = 0; e < 16; ++e) {
-      uint32_t bits = (wv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      float ax = __uint_as_float((bits & 0x7FFFu) << 16);
-      uint32_t nib = (uint32_t)exact_index(ax, t.tau[c]) | ((bits >> 12) & 8u);
-      o[e >> 3] |= nib << ((e & 7) * 4);
-    }
-    out.x = o[0]; out.y = o[1];
-  }
-  return out;
+  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16lo(wv[i]); x[2 * i + 1] = bf16hi(wv[i]); }
+  return nibbles16(x, c, t, mode);
 }
 
 constexpr int kUnits = 4;                // blocks per thread per batch (loads in flight)
@@ -205,6 +175,7 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
   const bool est = inv > 0.0f && inv < __builtin_inff();     // wave-uniform
   build_code_search(tp, s2);
   build_code_tables(t, s2, force_exact);    // syncs
+  const int mode = table_mode(t);
 
   while (pos.r < rows) {
     uint32_t wv[kUnits][8];
@@ -225,7 +196,7 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
         for (int i = 0; i < 8; ++i) m2 = absmax2(m2, wv[j][i]);
         const uint32_t P = max((uint32_t)m2.x, (uint32_t)m2.y);
         const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
-        const uint2 q = quantize_block(wv[j], c, t);
+        const uint2 q = quantize_block(wv[j], c, t, mode);
         *reinterpret_cast<uint2*>(packed + pos.r * (k >> 1) + pos.g * 8) = q;
         codes[pos.r * nb + pos.g] = (uint8_t)c;
       }

@@ -95,31 +95,17 @@ __device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
 }
 
 // e = w - q d for the 16 elements at code c (lane-varying), exact quantization.
-__device__ __forceinline__ void block_error(const float* wv, int c, const CodeTables& t, float* e) {
+__device__ __forceinline__ void block_error(const float* wv, int c, const CodeTables& t, int mode, float* e) {
   const float d = t.d[c];
+  const uint2 nb = nibbles16(wv, c, t, mode);
   float q[16];
-  if (is_cert(t, c)) {
-    const float r = t.r[c];
 #pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      uint32_t nb = cvt_fp4x2<0>(0u, wv[i] * r, wv[i + 1] * r);
-      nb = cvt_fp4x2<1>(nb, wv[i + 2] * r, wv[i + 3] * r);
-      fp4x2_to_f32<0>(nb, q[i], q[i + 1]);
-      fp4x2_to_f32<1>(nb, q[i + 2], q[i + 3]);
-    }
-  } else if (is_cert2(t, c)) {
-    const float rh = t.rh[c], rl = t.rl[c];
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      uint32_t nb = cvt_fp4x2<0>(0u, quot1(wv[i], d, rh, rl), quot1(wv[i + 1], d, rh, rl));
-      nb = cvt_fp4x2<1>(nb, quot1(wv[i + 2], d, rh, rl), quot1(wv[i + 3], d, rh, rl));
-      fp4x2_to_f32<0>(nb, q[i], q[i + 1]);
-      fp4x2_to_f32<1>(nb, q[i + 2], q[i + 3]);
-    }
-  } else {
-    const float* tau = t.tau[c];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = __builtin_copysignf(e2m1_mag(exact_index(fabsf(wv[i]), tau)), wv[i]);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = h ? nb.y : nb.x;
+    fp4x2_to_f32<0>(w, q[8 * h + 0], q[8 * h + 1]);
+    fp4x2_to_f32<1>(w, q[8 * h + 2], q[8 * h + 3]);
+    fp4x2_to_f32<2>(w, q[8 * h + 4], q[8 * h + 5]);
+    fp4x2_to_f32<3>(w, q[8 * h + 6], q[8 * h + 7]);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) e[i] = fmaf(-q[i], d, wv[i]);
@@ -139,40 +125,6 @@ __device__ __forceinline__ float quad_form(const float* e, const float* Hg, cons
   return 2.0f * acc;
 }
 
-// Nibbles of the block at code c (same quantization paths as block_error).
-__device__ __forceinline__ uint2 block_nibbles(const float* wv, int c, const CodeTables& t) {
-  uint32_t o[2] = {0u, 0u};
-  if (is_cert(t, c)) {
-    const float r = t.r[c];
-#pragma unroll
-    for (int i = 0; i < 16; i += 8) {
-      uint32_t nb = cvt_fp4x2<0>(0u, wv[i] * r, wv[i + 1] * r);
-      nb = cvt_fp4x2<1>(nb, wv[i + 2] * r, wv[i + 3] * r);
-      nb = cvt_fp4x2<2>(nb, wv[i + 4] * r, wv[i + 5] * r);
-      nb = cvt_fp4x2<3>(nb, wv[i + 6] * r, wv[i + 7] * r);
-      o[i >> 3] = nb;
-    }
-  } else if (is_cert2(t, c)) {
-    const float d = t.d[c], rh = t.rh[c], rl = t.rl[c];
-#pragma unroll
-    for (int i = 0; i < 16; i += 8) {
-      uint32_t nb = cvt_fp4x2<0>(0u, quot1(wv[i], d, rh, rl), quot1(wv[i + 1], d, rh, rl));
-      nb = cvt_fp4x2<1>(nb, quot1(wv[i + 2], d, rh, rl), quot1(wv[i + 3], d, rh, rl));
-      nb = cvt_fp4x2<2>(nb, quot1(wv[i + 4], d, rh, rl), quot1(wv[i + 5], d, rh, rl));
-      nb = cvt_fp4x2<3>(nb, quot1(wv[i + 6], d, rh, rl), quot1(wv[i + 7], d, rh, rl));
-      o[i >> 3] = nb;
-    }
-  } else {
-    const float* tau = t.tau[c];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t nib = (uint32_t)exact_index(fabsf(wv[i]), tau) | (__builtin_signbitf(wv[i]) ? 8u : 0u);
-      o[i >> 3] |= nib << ((i & 7) * 4);
-    }
-  }
-  return make_uint2(o[0], o[1]);
-}
-
 __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t k,
                                                          int64_t ldw, const float* __restrict__ H,
                                                          const float* __restrict__ scale2, int64_t rows_per_wg,
@@ -185,6 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
   const float s2 = *scale2;
   build_code_search(tp, s2);
   build_code_tables(t, s2, force_exact);                     // syncs
+  const int mode = table_mode(t);
 
   const int64_t groups = k >> 4;
   const int lane = threadIdx.x & 63;
@@ -239,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
     c0 = c0 < 1 ? 1 : (c0 > kCodes - 1 ? kCodes - 1 : c0);
     {
       float e[16];
-      block_error(wv, c0, t, e);
+      block_error(wv, c0, t, mode, e);
       const float cc = quad_form(e, Hg, hh);
       if (!done && cc < best) { best = cc; bestc = c0; }      // c0 > 0: a tie keeps code 0
     }
@@ -281,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
       }
       if (!__any(!done)) break;                              // wave-uniform exit; at most 126 steps
       float e[16];
-      block_error(wv, next, t, e);
+      block_error(wv, next, t, mode, e);
       const float cc = quad_form(e, Hg, hh);
       if (!done) {
         if (next < lo) lo = next; else hi = next;
@@ -289,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
       }
     }
     if (valid) {
-      const uint2 nb = block_nibbles(wv, bestc, t);
+      const uint2 nb = nibbles16(wv, bestc, t, mode);
       *reinterpret_cast<uint2*>(packed + r * (k >> 1) + g * 8) = nb;
       codes[r * groups + g] = (uint8_t)bestc;
       if (cost) cost[r * groups + g] = best;
