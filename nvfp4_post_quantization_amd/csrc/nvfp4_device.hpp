@@ -250,45 +250,48 @@ __device__ __forceinline__ int exact_index(float ax, const float* tau) {
   return idx;
 }
 
-// Packed E2M1 nibbles of 16 values at code c on one level (element 2i in the
+// Packed E2M1 nibbles of 8 values at code c on one level (element 2i in the
 // low nibble of byte i): levels 0-2 through the FP4 convert (RNE, saturating)
 // of the certified fast quotient, level 3 by the exact thresholds.
 template <int LEVEL>
-__device__ __forceinline__ uint2 nibbles16_level(const float* x, int c, const CodeTables& t) {
-  uint32_t o[2] = {0u, 0u};
+__device__ __forceinline__ uint32_t nibbles8_level(const float* x, int c, const CodeTables& t) {
   if constexpr (LEVEL == 3) {
     const float* tau = t.tau[c];
+    uint32_t o = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const uint32_t nib = (uint32_t)exact_index(fabsf(x[i]), tau) | (__builtin_signbitf(x[i]) ? 8u : 0u);
-      o[i >> 3] |= nib << ((i & 7) * 4);
+      o |= nib << (i * 4);
     }
+    return o;
   } else {
     const float d = t.d[c], rh = LEVEL == 0 ? t.r[c] : t.rh[c], rl = t.rl[c];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float* v = x + 8 * h;
-      uint32_t nb = cvt_fp4x2<0>(0u, fast_quot(v[0], d, rh, rl, LEVEL), fast_quot(v[1], d, rh, rl, LEVEL));
-      nb = cvt_fp4x2<1>(nb, fast_quot(v[2], d, rh, rl, LEVEL), fast_quot(v[3], d, rh, rl, LEVEL));
-      nb = cvt_fp4x2<2>(nb, fast_quot(v[4], d, rh, rl, LEVEL), fast_quot(v[5], d, rh, rl, LEVEL));
-      nb = cvt_fp4x2<3>(nb, fast_quot(v[6], d, rh, rl, LEVEL), fast_quot(v[7], d, rh, rl, LEVEL));
-      o[h] = nb;
-    }
+    uint32_t nb = cvt_fp4x2<0>(0u, fast_quot(x[0], d, rh, rl, LEVEL), fast_quot(x[1], d, rh, rl, LEVEL));
+    nb = cvt_fp4x2<1>(nb, fast_quot(x[2], d, rh, rl, LEVEL), fast_quot(x[3], d, rh, rl, LEVEL));
+    nb = cvt_fp4x2<2>(nb, fast_quot(x[4], d, rh, rl, LEVEL), fast_quot(x[5], d, rh, rl, LEVEL));
+    nb = cvt_fp4x2<3>(nb, fast_quot(x[6], d, rh, rl, LEVEL), fast_quot(x[7], d, rh, rl, LEVEL));
+    return nb;
   }
-  return make_uint2(o[0], o[1]);
 }
 
-// Nibbles of 16 values at code c (lane-varying).  mode = t.mode, read once
+// Nibbles of 8 values at code c (lane-varying).  mode = t.mode, read once
 // per kernel into a scalar register: modes 0 and 1 take one level for every
 // code (a uniform branch); mode 2 dispatches per code.
-__device__ __forceinline__ uint2 nibbles16(const float* x, int c, const CodeTables& t, int mode) {
-  if (mode == 0) return nibbles16_level<0>(x, c, t);
-  if (mode == 1) return nibbles16_level<1>(x, c, t);
+__device__ __forceinline__ uint32_t nibbles8(const float* x, int c, const CodeTables& t, int mode) {
+  if (mode == 0) return nibbles8_level<0>(x, c, t);
+  if (mode == 1) return nibbles8_level<1>(x, c, t);
   const int lvl = code_level(t, c);
-  if (lvl == 0) return nibbles16_level<0>(x, c, t);
-  if (lvl == 1) return nibbles16_level<1>(x, c, t);
-  if (lvl == 2) return nibbles16_level<2>(x, c, t);
-  return nibbles16_level<3>(x, c, t);
+  if (lvl == 0) return nibbles8_level<0>(x, c, t);
+  if (lvl == 1) return nibbles8_level<1>(x, c, t);
+  if (lvl == 2) return nibbles8_level<2>(x, c, t);
+  return nibbles8_level<3>(x, c, t);
+}
+
+// The same for 16 values (two nibble words).
+__device__ __forceinline__ uint2 nibbles16(const float* x, int c, const CodeTables& t, int mode) {
+  if (mode == 0) return make_uint2(nibbles8_level<0>(x, c, t), nibbles8_level<0>(x + 8, c, t));
+  if (mode == 1) return make_uint2(nibbles8_level<1>(x, c, t), nibbles8_level<1>(x + 8, c, t));
+  return make_uint2(nibbles8(x, c, t, 2), nibbles8(x + 8, c, t, 2));
 }
 
 __device__ __forceinline__ int table_mode(const CodeTables& t) { return __builtin_amdgcn_readfirstlane(t.mode); }

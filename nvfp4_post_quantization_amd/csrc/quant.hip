@@ -64,7 +64,7 @@ __device__ __forceinline__ u16x2 absmax2(u16x2 m, uint32_t v) {
 }
 
 constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per thread
-constexpr int kAmaxGrid = 512;          // two workgroups per CU (measured best for streaming)
+constexpr int kAmaxGrid = 256;          // one workgroup per CU: fewest same-address atomics (measured best)
 
 __global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                           uint32_t* acc) {
