@@ -27,6 +27,7 @@
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
+
 namespace nvfp4 {
 
 namespace {
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void cast_kmax_kernel(const uint8_t* __re
     if (aligned && c0 + kKmaxChunk <= per_group) {
       uint4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(e + c0 + 16 * (threadIdx.x + kThreads * u));
+      for (int u = 0; u < 4; ++u) v[u] = ld_nt4(e + c0 + 16 * (threadIdx.x + kThreads * u));
 #pragma unroll
       for (int u = 0; u < 4; ++u) m = max(m, max_valid16(v[u]));
     } else {
@@ -217,12 +218,12 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
   int64_t c0 = (int64_t)blockIdx.x * kCodesChunk;
   auto whole = [&](int64_t c) { return aligned && c + kCodesChunk <= per_group; };
   uint2 e = make_uint2(0u, 0u);
-  if (c0 < per_group && whole(c0)) e = *reinterpret_cast<const uint2*>(e8m0 + base + c0 + 8 * threadIdx.x);
+  if (c0 < per_group && whole(c0)) e = ld_nt2(e8m0 + base + c0 + 8 * threadIdx.x);
   for (; c0 < per_group; c0 += step) {
     if (whole(c0)) {
       const uint2 cur = e;
       const int64_t n0 = c0 + step;
-      if (n0 < per_group && whole(n0)) e = *reinterpret_cast<const uint2*>(e8m0 + base + n0 + 8 * threadIdx.x);
+      if (n0 < per_group && whole(n0)) e = ld_nt2(e8m0 + base + n0 + 8 * threadIdx.x);
       const int64_t j = base + c0 + 8 * threadIdx.x;
       const uint32_t ew[2] = {cur.x, cur.y};
       uint32_t c[4];

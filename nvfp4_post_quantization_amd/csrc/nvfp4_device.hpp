@@ -55,6 +55,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Non-temporal loads for data read exactly once (streamed inputs): they keep
+// it from displacing cached data.
+typedef uint32_t ntu32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t ntu32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt4(const void* p) {
+  const ntu32x4 v = __builtin_nontemporal_load(reinterpret_cast<const ntu32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt2(const void* p) {
+  const ntu32x2 v = __builtin_nontemporal_load(reinterpret_cast<const ntu32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // Two fp32 -> two FP4 codes in byte `sel` of `old` (element a in the low nibble).
 template <int SEL>
 __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {

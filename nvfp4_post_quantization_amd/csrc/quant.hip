@@ -19,6 +19,7 @@
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
+
 namespace nvfp4 {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __rest
   for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = x16[i + u * stride];
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = ld_nt4(x16 + i + u * stride);
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
       m2 = absmax2(m2, v[u].x); m2 = absmax2(m2, v[u].y); m2 = absmax2(m2, v[u].z); m2 = absmax2(m2, v[u].w);
@@ -163,8 +164,8 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
     for (int j = 0; j < kUnits; ++j) {
       if (p.r < rows) {
         const uint4* src = reinterpret_cast<const uint4*>(x + p.r * ldx + p.g * 16);
-        v[j][0] = src[0];
-        v[j][1] = src[1];
+        v[j][0] = ld_nt4(src);
+        v[j][1] = ld_nt4(src + 1);
       }
       p.advance(dr, dg, nb);
     }
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
       if (q.r < rows) {
-        p[j] = *reinterpret_cast<const uint32_t*>(packed + q.r * (k >> 1) + q.g * 4);
+        p[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(packed + q.r * (k >> 1) + q.g * 4));
         cd[j] = codes[q.r * (k >> 4) + (q.g >> 1)];
       }
       q.advance(dr, dg, nh);
