@@ -31,7 +31,9 @@ Readings where the pages are silent are marked "reading:" in the docstrings.
 Parity unpinned (readings the pages cannot confirm; no worked example is
 printed): the argmin tie-break (lowest code), the sign of a zero nibble, the
 exact-quotient rounding rule, nibble order within a byte, the clamp of a
-nonzero block's code to 0x01, and the synthetic input recipes.
+nonzero block's code to 0x01, the synthetic input recipes, and (for the W4A4
+Hessian variant) that the layer input is taken after its activation
+quantizer.
 """
 from .formats import (
     E2M1_MAGNITUDES, E4M3_VALUES, e2m1_decode, e2m1_encode, e4m3_value,
@@ -40,7 +42,7 @@ from .formats import (
 )
 from .nvfp4 import (
     tensor_scale, hessian, block_scale, quantize_at_code, block_cost,
-    sweep_costs, scale_sweep, max_code, quantize_dynamic, dequant,
+    sweep_costs, scale_sweep, max_code, quantize_dynamic, dequant, hessian_fakequant,
 )
 from .mxcast import mxfp4_to_nvfp4, mxfp4_dequant
 
@@ -49,6 +51,6 @@ __all__ = [
     "e4m3_encode_ratio", "e8m0_value", "bf16_bits_to_f64", "f64_to_bf16_bits", "f32",
     "pack_nibbles", "unpack_nibbles",
     "tensor_scale", "hessian", "block_scale", "quantize_at_code", "block_cost",
-    "sweep_costs", "scale_sweep", "max_code", "quantize_dynamic", "dequant",
+    "sweep_costs", "scale_sweep", "max_code", "quantize_dynamic", "dequant", "hessian_fakequant",
     "mxfp4_to_nvfp4", "mxfp4_dequant",
 ]

@@ -154,3 +154,13 @@ def dequant(packed, codes, s2):
     d = block_scale(codes, s2)                       # [rows, K/16]
     v = e2m1_decode(nib).reshape(rows, k // BLOCK, BLOCK) * d[..., None]
     return f64_to_bf16_bits(f32(v).reshape(rows, k))
+
+
+def hessian_fakequant(x_bits, s2, h_init=None):
+    """Step 2 for a W4A4 calibration (reading: the layer input is seen after
+    its dynamic NVFP4 quantizer): H_g += Xh_g^T Xh_g with Xh the bf16 output
+    of the two-DQ chain applied to the dynamic per-16 quantization of X at
+    tensor scale s2 (pi05 flow note §3.4-§3.5, §5.4; Coder390 note §2 step 2).
+    """
+    packed, codes = quantize_dynamic(x_bits, s2)
+    return hessian(dequant(packed, codes, s2), h_init=h_init)

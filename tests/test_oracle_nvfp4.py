@@ -249,3 +249,29 @@ def test_dequant_chain_against_torch_decode():
     y = (val.view(32, 8, 16) * d[..., None]).reshape(32, 128)          # DQ2 in FP32
     ref = y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(out, ref)
+
+
+def test_hessian_fakequant_identity_and_zero():
+    """W4A4 Hessian variant: an input that the dynamic quantizer reproduces
+    exactly (every element e2m1 * d at its block's own max-based code) gives
+    the plain Hessian; a zero tensor scale quantizes everything to zero."""
+    rng = np.random.default_rng(31)
+    s2 = 2.0 ** -8
+    rows = []
+    for t in range(40):
+        code = int(rng.integers(8, 120))
+        d = float(F.E4M3_VALUES[code]) * s2
+        q = rng.choice(F.E2M1_MAGNITUDES, 32) * rng.choice([-1.0, 1.0], 32)
+        q[0], q[16] = 6.0, -6.0                       # each block's max is 6 d: the block keeps this code
+        rows.append(q * d)
+    x = datagen.f32_to_bf16_bits(np.array(rows).astype(np.float32))
+    assert np.array_equal(F.bf16_bits_to_f64(x), np.array(rows)), "test inputs must be bf16-exact"
+    assert np.array_equal(N.hessian_fakequant(x, s2), N.hessian(x))
+    y = datagen.f32_to_bf16_bits(rng.standard_normal((40, 32)).astype(np.float32))
+    assert np.array_equal(N.hessian_fakequant(y, 0.0), np.zeros((2, 16, 16)))
+    # a generic input differs from the plain Hessian, and stays PSD and symmetric
+    _, s2y = N.tensor_scale(y)
+    hf = N.hessian_fakequant(y, s2y)
+    assert not np.array_equal(hf, N.hessian(y))
+    assert np.array_equal(hf, hf.transpose(0, 2, 1))
+    assert np.min(np.linalg.eigvalsh(hf)) >= -1e-9 * np.max(np.abs(hf))
