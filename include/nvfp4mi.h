@@ -112,6 +112,30 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Step 2 for a W4A4 calibration, where the Linear's input passes through its
+ * dynamic NVFP4 quantizer ("Coder390 NVFP4 校正（校准）方式" §3, the W4A4
+ * tier; quantizer and two-level dequantization of "NVFP4 量化流程说明"
+ * §3.4-§3.5): for every group g of 16 input channels,
+ *   H[g] += sum_t xh[t, 16g:16g+16]^T xh[t, 16g:16g+16],
+ *   xh = bf16 output of nvfp4_dequant(nvfp4_quantize_dynamic(x, scale2))
+ * element for element, without writing the quantized activations to memory
+ * (each 16-element block is quantized and dequantized in registers between
+ * the load of x and the contraction).  Accumulation and reduction order are
+ * those of nvfp4_hessian_accum, which it shares the workspace query with.
+ *
+ * x, tokens, k, ldx, H, workspace, workspace_bytes, stream: as for
+ *            nvfp4_hessian_accum.
+ * scale2     device float[1]: the activations' tensor scale (step 1 run
+ *            beforehand, e.g. nvfp4_compute_scale2 over calibration inputs).
+ * amax_inout device float[1] or NULL: raised to max(*amax_inout, max |x|)
+ *            over the RAW (unquantized) input, for the next scale_2.
+ * Errors: as for nvfp4_hessian_accum, plus NULL_ARG for scale2.
+ */
+int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
+                           const float* scale2, float* H, float* amax_inout,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Step 3, the Hessian-weighted block-scale sweep (fp8_scale_sweep,
  * "Coder390 NVFP4 校正（校准）方式" §2 step 3).  For every block b = (row r,
  * group g) of 16 weights w and every finite E4M3 code c in 0x00..0x7E:

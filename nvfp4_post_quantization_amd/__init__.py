@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
-    "hessian_accum", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
+    "hessian_accum", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
@@ -35,6 +35,8 @@ _SIGS = {
     "nvfp4_hessian_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_hessian_accum": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                            ctypes.c_size_t, _c_void_p]),
+    "nvfp4_hessian_accum_fq": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                              _c_void_p, ctypes.c_size_t, _c_void_p]),
     "nvfp4_scale_sweep": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                          _c_void_p, _c_void_p, _c_void_p]),
     "nvfp4_quantize_dynamic": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
@@ -144,6 +146,31 @@ def hessian_accum(x: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = 
     _check("nvfp4_hessian_accum", load().nvfp4_hessian_accum(
         x.data_ptr(), tokens, k, ldx, H.data_ptr(), amax.data_ptr() if amax is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return H
+
+
+def hessian_accum_fq(x: torch.Tensor, scale2: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 form of hessian_accum: H += block-diagonal Xh^T Xh, where Xh is x
+    after the dynamic NVFP4 quantizer at tensor scale scale2 (f32[1]) and the
+    two-level dequantization, computed in one pass over x.  amax, if given, is
+    raised to the raw max|x|."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(H, torch.float32, "H")
+    _dev(scale2, torch.float32, "scale2")
+    tokens, k = x.shape
+    if H.numel() != (k // 16) * 256 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [k/16, 16, 16] tensor")
+    ldx = _row_major(x, "x")
+    need = hessian_workspace_bytes(tokens, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    if amax is not None:
+        _dev(amax, torch.float32, "amax")
+    _check("nvfp4_hessian_accum_fq", load().nvfp4_hessian_accum_fq(
+        x.data_ptr(), tokens, k, ldx, scale2.data_ptr(), H.data_ptr(),
+        amax.data_ptr() if amax is not None else None, workspace.data_ptr(), workspace.numel(), _stream(x)))
     return H
 
 

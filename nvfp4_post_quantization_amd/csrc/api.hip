@@ -67,8 +67,9 @@ size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k) {
   return hessian_workspace_bytes(tokens, k);
 }
 
-int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax_inout,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+// Shared validation of the two Hessian entry points.
+static int check_hessian(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* H,
+                         const void* workspace, size_t workspace_bytes) {
   int st = check_matrix(tokens, k, ldx, 2);
   if (st) return st;
   if (k % 16) return NVFP4_ERR_BAD_SHAPE;
@@ -79,7 +80,23 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (need && !workspace) return NVFP4_ERR_NULL_ARG;
   if (!aligned16(H) || !aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  return NVFP4_OK;
+}
+
+int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax_inout,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_hessian(x, tokens, k, ldx, H, workspace, workspace_bytes);
+  if (st || tokens == 0) return st;
   return launch_hessian_accum(x, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
+}
+
+int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
+                           float* amax_inout, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_hessian(x, tokens, k, ldx, H, workspace, workspace_bytes);
+  if (st) return st;
+  if (!scale2) return NVFP4_ERR_NULL_ARG;
+  if (tokens == 0) return NVFP4_OK;
+  return launch_hessian_accum_fq(x, tokens, k, ldx, scale2, H, amax_inout, workspace, as_stream(stream));
 }
 
 int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,

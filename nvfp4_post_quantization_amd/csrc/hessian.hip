@@ -21,6 +21,9 @@
 //    workgroups to H in fp64, in workgroup order (deterministic).
 // Optionally the running max |x| (calibration step 1) is taken from the MFMA
 // operands, which together hold every element of a tile.
+// The W4A4 variant (nvfp4_hessian_accum_fq) accumulates the Hessian of the
+// fake-quantized input instead: each lane pair quantizes its 16-element
+// block in registers before the tile goes to LDS.
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -73,12 +76,65 @@ __device__ __forceinline__ u16x2 abs_max2(u16x2 m, uint32_t v) {
   return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v) & u16x2{0x7FFF, 0x7FFF});
 }
 
-__global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Fake quantization of 8 bf16 values, one half of a 16-element block (lanes
+// l and l^1 hold the two halves): the dynamic quantizer's code from the block
+// max, E2M1 at that code, then the two-DQ chain back to bf16.  Returns the
+// block's raw max |x| pattern in P.
+__device__ __forceinline__ uint4 fake_quant8(uint4 v, const CodeTables& t, const int32_t* tp, float s2, float inv,
+                                             bool est, int mode, uint32_t& P) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  u16x2 m2 = u16x2{0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m2 = abs_max2(m2, wv[i]);
+  P = max((uint32_t)m2.x, (uint32_t)m2.y);
+  P = max(P, (uint32_t)__shfl_xor((int)P, 1));
+  const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
+  float xv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { xv[2 * i] = bf16lo(wv[i]); xv[2 * i + 1] = bf16hi(wv[i]); }
+  const uint32_t nb = nibbles8(xv, c, t, mode);
+  const float d = t.d[c];
+  float a0, b0, a1, b1, a2, b2, a3, b3;
+  fp4x2_to_f32<0>(nb, a0, b0);
+  fp4x2_to_f32<1>(nb, a1, b1);
+  fp4x2_to_f32<2>(nb, a2, b2);
+  fp4x2_to_f32<3>(nb, a3, b3);
+  const f32x2 y0 = {a0 * d, b0 * d}, y1 = {a1 * d, b1 * d}, y2 = {a2 * d, b2 * d}, y3 = {a3 * d, b3 * d};
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(y0, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(y1, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(y3, bf16x2)));
+}
+
+// FQ = false: H += X^T X.  FQ = true (W4A4 calibration): H += Xh^T Xh with
+// Xh = DQ(Q(X)) at the activations' tensor scale, quantized in registers
+// between the load and the LDS store; the fused amax is then taken from the
+// raw block maxima.
+template <bool FQ>
+__global__ __launch_bounds__(kThreads, FQ ? 3 : 6) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
                                                                     int64_t k, int64_t ldx, int64_t tiles,
                                                                     int64_t total, int64_t wgs, int64_t segs,
                                                                     int64_t slabs, int64_t streams,
-                                                                    float* __restrict__ ws, float* amax) {
+                                                                    float* __restrict__ ws, float* amax,
+                                                                    const float* __restrict__ scale2,
+                                                                    int force_exact) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
+  __shared__ CodeTables t;
+  __shared__ int32_t tp[128];
+  float s2 = 0.0f, inv = 0.0f;
+  bool est = false;
+  int mode = 0;
+  if constexpr (FQ) {
+    s2 = *scale2;
+    inv = (float)(1.0 / (6.0 * (double)s2));
+    est = inv > 0.0f && inv < __builtin_inff();
+    build_code_search(tp, s2);
+    build_code_tables(t, s2, force_exact);                 // syncs
+    mode = table_mode(t);
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -138,7 +194,13 @@ __global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int R = lr + 16 * u;
-        *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = buf[u];
+        uint4 val = buf[u];
+        if constexpr (FQ) {
+          uint32_t P;
+          val = fake_quant8(val, t, tp, s2, inv, est, mode, P);
+          amx = __builtin_elementwise_max(amx, u16x2{(uint16_t)P, 0});
+        }
+        *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = val;
       }
       __syncthreads();
       if (i + 2 < ntiles) load_tile(buf, i + 2);
@@ -155,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint
             const int R = 32 * m + 8 * q + e;
             v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
           }
-          if (amax) {
+          if (!FQ && amax) {
             const u32x4 d = __builtin_bit_cast(u32x4, v);
             amx = abs_max2(abs_max2(abs_max2(abs_max2(amx, d.x), d.y), d.z), d.w);
           }
@@ -272,18 +334,30 @@ size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
   return (size_t)(p.wgs * p.segs) * kSlabGroups * 256u * sizeof(float);
 }
 
-int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
-                         void* workspace, hipStream_t s) {
+template <bool FQ>
+static int launch_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
+                        float* amax, void* workspace, hipStream_t s) {
   const Plan p = plan(tokens, k);
   if (p.wgs == 0) return NVFP4_OK;
   float* ws = static_cast<float*>(workspace);
-  hessian_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
-                                                                p.slabs, p.streams, ws, amax);
+  hessian_partial_kernel<FQ><<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs,
+                                                                    p.segs, p.slabs, p.streams, ws, amax, scale2,
+                                                                    FQ ? force_exact_flag() : 0);
   int st = launch_status("hessian_partial_kernel");
   if (st) return st;
   hessian_reduce_kernel<<<(unsigned)(k / 16), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles, p.total,
                                                             p.wgs, p.segs, reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
+}
+
+int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
+                         void* workspace, hipStream_t s) {
+  return launch_accum<false>(x, tokens, k, ldx, nullptr, H, amax, workspace, s);
+}
+
+int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
+                            float* amax, void* workspace, hipStream_t s) {
+  return launch_accum<true>(x, tokens, k, ldx, scale2, H, amax, workspace, s);
 }
 
 }  // namespace nvfp4

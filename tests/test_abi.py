@@ -36,7 +36,7 @@ def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) == {
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
-        "nvfp4_hessian_accum", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
+        "nvfp4_hessian_accum", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast",
     }
     for n in names:
@@ -81,6 +81,22 @@ def test_hessian_validation(lib):
     assert f(P, 16, 32, 32, P, None, None, need, None) == NULL
     assert f(P, 0, 32, 32, P, None, None, 0, None) == OK                  # nothing to do
     assert f(P, 1 << 62, 32, 1 << 40, P, None, P, 1 << 20, None) == SHAPE   # overflow
+
+
+def test_hessian_fq_validation(lib):
+    f = lib.nvfp4_hessian_accum_fq
+    need = lib.nvfp4_hessian_workspace_bytes(16, 32)
+    assert f(P, 16, 24, 24, P, P, None, P, 1 << 20, None) == SHAPE         # k % 16
+    assert f(P, 16, 32, 16, P, P, None, P, 1 << 20, None) == SHAPE         # ld < k
+    assert f(P, 16, 32, 32, None, P, None, P, need, None) == NULL          # scale2
+    assert f(P, 16, 32, 32, P, None, None, P, need, None) == NULL          # H
+    assert f(None, 16, 32, 32, P, P, None, P, need, None) == NULL
+    assert f(P + 2, 16, 32, 32, P, P, None, P, need, None) == ALIGN
+    assert f(P, 16, 32, 32, P, P + 4, None, P, need, None) == ALIGN        # H
+    assert f(P, 16, 32, 32, P, P, None, P + 8, need, None) == ALIGN        # workspace
+    assert f(P, 16, 32, 32, P, P, None, P, need - 1, None) == WS
+    assert f(P, 0, 32, 32, P, P, None, None, 0, None) == OK                # nothing to do
+    assert f(P, 0, 32, 32, None, P, None, None, 0, None) == NULL           # scale2 even when empty
 
 
 def test_sweep_quant_dequant_validation(lib):
