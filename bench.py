@@ -13,6 +13,9 @@ inputs:
   * activations X [8192, 4096]: a1 amax, a4 dynamic NVFP4 quantization and
     a5 the dequant round trip;
   * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast.
+After the timed steps, the W4A4 form of a2 (Hessian of the fake-quantized
+calibration streams) is timed on its own and reported under
+stages.next_w4a4_hessian; it is not part of the step.
 
 The headline value is weight blocks swept per second of whole-step time.
 Per-stage times come from HIP events on the stream the library launches on.
@@ -224,6 +227,37 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "per_launch": f"{x_bytes / 32 / 1e9:.4f} GB avg, {per_launch_s * 1e3:.4f} ms avg"}
     roof["traffic"] = traffic_from_profiles(roof["kernel"])
+
+    # W4A4 form of a2, outside the step: the Hessian of the fake-quantized
+    # calibration streams (activation scale_2 from max calibration of each
+    # stream's first chunk), 32 chunk calls per pass
+    s2a = {s: torch.zeros(1, **f32) for s in (0, 1)}
+    Hq = {s: torch.zeros_like(H[s]) for s in (0, 1)}
+    for s in (0, 1):
+        chk("scale2", lib.nvfp4_compute_scale2(X[s][0].data_ptr(), X[s][0].numel(), s2a[s].data_ptr(), None, sptr))
+
+    def fq_pass():
+        for s in (0, 1):
+            Hq[s].zero_()
+            for x in X[s]:
+                chk("hessian_fq", lib.nvfp4_hessian_accum_fq(x.data_ptr(), x.shape[0], x.shape[1], x.shape[1],
+                                                             s2a[s].data_ptr(), Hq[s].data_ptr(), None,
+                                                             ws.data_ptr(), ws.numel(), sptr))
+
+    fq_pass()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fq_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fq_ms = e0.elapsed_time(e1) / args.steps
+    fq_gbs = x_bytes / (fq_ms / 1e3) / 1e9
+    stage_rep["next_w4a4_hessian"] = {
+        "outside_step": True, "ms_per_pass": round(fq_ms, 4), "launches_per_pass": 32,
+        "algorithmic_GB": round(x_bytes / 1e9, 4), "GBps": round(fq_gbs, 1),
+        "frac_hbm_peak": round(fq_gbs / HBM_PEAK_GBS, 4),
+        "kernel": "hessian_fq_partial_kernel+hessian_reduce_kernel"}
 
     if args.copy_probe:
         # an elementwise kernel of known traffic (4 GiB read + 4 GiB written per

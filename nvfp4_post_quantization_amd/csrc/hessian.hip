@@ -36,6 +36,7 @@ constexpr int kSlabCols = kSlabGroups * 16;
 constexpr int kTile = 64;                 // tokens per LDS tile
 constexpr int kThreads = 256;
 constexpr int kTargetWgs = 512;           // two workgroups on each of 256 CUs (measured best)
+constexpr int kTargetWgsFq = 1024;        // fake-quant variant: ALU-heavier, four per CU hide more latency
 constexpr int kReduceParts = 4;           // workgroup sub-ranges summed in parallel by the reduce
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -57,13 +58,13 @@ struct Plan {
   int64_t slabs, tiles, total, wgs, segs, streams;
 };
 
-Plan plan(int64_t tokens, int64_t k) {
+Plan plan(int64_t tokens, int64_t k, int64_t target) {
   Plan p;
   p.slabs = cdiv(k / 16, kSlabGroups);
   p.tiles = cdiv(tokens, kTile);
   p.total = p.slabs * p.tiles;
-  p.streams = p.slabs < kTargetWgs ? kTargetWgs / p.slabs : 1;
-  p.wgs = p.slabs < kTargetWgs ? p.slabs * p.streams : kTargetWgs;
+  p.streams = p.slabs < target ? target / p.slabs : 1;
+  p.wgs = p.slabs < target ? p.slabs * p.streams : target;
   if (p.wgs > p.total) p.wgs = p.total;
   p.segs = p.wgs > 0 ? cdiv(cdiv(p.total, p.wgs), p.tiles) + 1 : 0;
   return p;
@@ -79,62 +80,78 @@ __device__ __forceinline__ u16x2 abs_max2(u16x2 m, uint32_t v) {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Fake quantization of 8 bf16 values, one half of a 16-element block (lanes
-// l and l^1 hold the two halves): the dynamic quantizer's code from the block
-// max, E2M1 at that code, then the two-DQ chain back to bf16.  Returns the
-// block's raw max |x| pattern in P.
-__device__ __forceinline__ uint4 fake_quant8(uint4 v, const CodeTables& t, const int32_t* tp, float s2, float inv,
-                                             bool est, int mode, uint32_t& P) {
-  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-  u16x2 m2 = u16x2{0, 0};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m2 = abs_max2(m2, wv[i]);
-  P = max((uint32_t)m2.x, (uint32_t)m2.y);
-  P = max(P, (uint32_t)__shfl_xor((int)P, 1));
-  const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
-  float xv[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { xv[2 * i] = bf16lo(wv[i]); xv[2 * i + 1] = bf16hi(wv[i]); }
-  const uint32_t nb = nibbles8(xv, c, t, mode);
-  const float d = t.d[c];
-  float a0, b0, a1, b1, a2, b2, a3, b3;
-  fp4x2_to_f32<0>(nb, a0, b0);
-  fp4x2_to_f32<1>(nb, a1, b1);
-  fp4x2_to_f32<2>(nb, a2, b2);
-  fp4x2_to_f32<3>(nb, a3, b3);
-  const f32x2 y0 = {a0 * d, b0 * d}, y1 = {a1 * d, b1 * d}, y2 = {a2 * d, b2 * d}, y3 = {a3 * d, b3 * d};
-  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(y0, bf16x2)),
-                    __builtin_bit_cast(uint32_t, __builtin_convertvector(y1, bf16x2)),
-                    __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2)),
-                    __builtin_bit_cast(uint32_t, __builtin_convertvector(y3, bf16x2)));
+// Quantizer state of the fake-quant variant: the code tables for the
+// activations' tensor scale, built once per workgroup in LDS.
+struct FqState {
+  const CodeTables* t;
+  const int32_t* tp;
+  float s2, inv;
+  bool est;     // inv = RN_f32(1 / (6 scale_2)) is finite and nonzero: arithmetic code estimate
+};
+
+// max over lanes l and l^1, which hold the two halves of one 16-element block
+__device__ __forceinline__ uint32_t pair_max(uint32_t p) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  return max(p, o);
 }
 
-// FQ = false: H += X^T X.  FQ = true (W4A4 calibration): H += Xh^T Xh with
-// Xh = DQ(Q(X)) at the activations' tensor scale, quantized in registers
-// between the load and the LDS store; the fused amax is then taken from the
-// raw block maxima.
-template <bool FQ>
-__global__ __launch_bounds__(kThreads, FQ ? 3 : 6) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
-                                                                    int64_t k, int64_t ldx, int64_t tiles,
-                                                                    int64_t total, int64_t wgs, int64_t segs,
-                                                                    int64_t slabs, int64_t streams,
-                                                                    float* __restrict__ ws, float* amax,
-                                                                    const float* __restrict__ scale2,
-                                                                    int force_exact) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
-  __shared__ CodeTables t;
-  __shared__ int32_t tp[128];
-  float s2 = 0.0f, inv = 0.0f;
-  bool est = false;
-  int mode = 0;
-  if constexpr (FQ) {
-    s2 = *scale2;
-    inv = (float)(1.0 / (6.0 * (double)s2));
-    est = inv > 0.0f && inv < __builtin_inff();
-    build_code_search(tp, s2);
-    build_code_tables(t, s2, force_exact);                 // syncs
-    mode = table_mode(t);
+// Fake quantization of the lane's four 8-value chunks of a tile, in place:
+// the dynamic quantizer's block code from the block max, E2M1 at that code,
+// then the two-level dequantization back to bf16 (RN_f32(e2m1 * d), then
+// RN_bf16).  QM is the E2M1 mode of the code tables (0 or 1: one certified
+// level for every code; 2: a level per code).  The chunks pass through each
+// phase together so that their table reads overlap.  amx collects the raw
+// block maxima (the fused amax of the unquantized input).
+template <int QM>
+__device__ __forceinline__ void fake_quant_tile(uint4* v, const FqState& q, u16x2& amx) {
+  uint32_t P[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u16x2 m2 = abs_max2(abs_max2(abs_max2(abs_max2(u16x2{0, 0}, v[u].x), v[u].y), v[u].z), v[u].w);
+    P[u] = pair_max(max((uint32_t)m2.x, (uint32_t)m2.y));
+    amx = __builtin_elementwise_max(amx, u16x2{(uint16_t)P[u], 0});
   }
+  int c[4];
+  if (q.est) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c[u] = block_code_est(P[u], q.tp, q.inv);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c[u] = block_code(P[u], q.tp, q.s2);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    float xv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { xv[2 * i] = bf16lo(wv[i]); xv[2 * i + 1] = bf16hi(wv[i]); }
+    uint32_t nb;
+    if constexpr (QM == 2) nb = nibbles8(xv, c[u], *q.t, 2);
+    else nb = nibbles8_level<QM>(xv, c[u], *q.t);
+    const float d = q.t->d[c[u]];
+    float a0, b0, a1, b1, a2, b2, a3, b3;
+    fp4x2_to_f32<0>(nb, a0, b0);
+    fp4x2_to_f32<1>(nb, a1, b1);
+    fp4x2_to_f32<2>(nb, a2, b2);
+    fp4x2_to_f32<3>(nb, a3, b3);
+    const f32x2 y0 = {a0 * d, b0 * d}, y1 = {a1 * d, b1 * d}, y2 = {a2 * d, b2 * d}, y3 = {a3 * d, b3 * d};
+    v[u] = make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(y0, bf16x2)),
+                      __builtin_bit_cast(uint32_t, __builtin_convertvector(y1, bf16x2)),
+                      __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2)),
+                      __builtin_bit_cast(uint32_t, __builtin_convertvector(y3, bf16x2)));
+  }
+}
+
+// One workgroup's share of the partial products.  QM < 0: H += X^T X (the
+// running max |x| is taken from the MFMA operands when want_amax).  QM >= 0
+// (W4A4 calibration): H += Xh^T Xh with Xh = DQ(Q(X)) at the activations'
+// tensor scale, quantized in registers between the load and the LDS store,
+// E2M1 mode QM.  Returns the lane's packed running max |x|.
+template <int QM>
+__device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, int64_t tokens, int64_t k, int64_t ldx,
+                                              int64_t tiles, int64_t total, int64_t wgs, int64_t segs, int64_t slabs,
+                                              int64_t streams, float* __restrict__ ws, bool want_amax,
+                                              uint16_t* tile, const FqState& fq) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -190,17 +207,12 @@ __global__ __launch_bounds__(kThreads, FQ ? 3 : 6) void hessian_partial_kernel(c
       }
     };
     auto consume = [&](uint4* buf, int i) {
+      if constexpr (QM >= 0) fake_quant_tile<QM>(buf, fq, amx);
       __syncthreads();                                 // previous tile fully read
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int R = lr + 16 * u;
-        uint4 val = buf[u];
-        if constexpr (FQ) {
-          uint32_t P;
-          val = fake_quant8(val, t, tp, s2, inv, est, mode, P);
-          amx = __builtin_elementwise_max(amx, u16x2{(uint16_t)P, 0});
-        }
-        *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = val;
+        *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = buf[u];
       }
       __syncthreads();
       if (i + 2 < ntiles) load_tile(buf, i + 2);
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(kThreads, FQ ? 3 : 6) void hessian_partial_kernel(c
             const int R = 32 * m + 8 * q + e;
             v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
           }
-          if (!FQ && amax) {
+          if (QM < 0 && want_amax) {
             const u32x4 d = __builtin_bit_cast(u32x4, v);
             amx = abs_max2(abs_max2(abs_max2(abs_max2(amx, d.x), d.y), d.z), d.w);
           }
@@ -247,19 +259,66 @@ __global__ __launch_bounds__(kThreads, FQ ? 3 : 6) void hessian_partial_kernel(c
     f = slab * tiles + t1;
   }
 
-  if (amax) {
-    __shared__ uint32_t part[kThreads / 64];
-    uint32_t am = max((uint32_t)amx.x, (uint32_t)amx.y);
+  return amx;
+}
+
+// atomic max of the workgroup's running max |x| into *amax (as fp32 bits)
+__device__ __forceinline__ void reduce_amax(u16x2 amx, float* amax) {
+  __shared__ uint32_t part[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t am = max((uint32_t)amx.x, (uint32_t)amx.y);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
-    if (lane == 0) part[wave] = am;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t r = 0;
-      for (int i = 0; i < kThreads / 64; ++i) r = max(r, part[i]);
-      if (r) atomicMax(reinterpret_cast<uint32_t*>(amax), r << 16);
-    }
+  for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+  if (lane == 0) part[wave] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kThreads / 64; ++i) r = max(r, part[i]);
+    if (r) atomicMax(reinterpret_cast<uint32_t*>(amax), r << 16);
   }
+}
+
+__global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
+                                                                       int64_t k, int64_t ldx, int64_t tiles,
+                                                                       int64_t total, int64_t wgs, int64_t segs,
+                                                                       int64_t slabs, int64_t streams,
+                                                                       float* __restrict__ ws, float* amax) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
+  const FqState q{};
+  const u16x2 amx = partial_body<-1>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws,
+                                     amax != nullptr, tile, q);
+  if (amax) reduce_amax(amx, amax);
+}
+
+// The fake-quant variant: tables first, then one loop per E2M1 mode (the
+// mode is uniform over the launch, so only one loop's code runs).
+__global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const uint16_t* __restrict__ x,
+                                                                          int64_t tokens, int64_t k, int64_t ldx,
+                                                                          int64_t tiles, int64_t total, int64_t wgs,
+                                                                          int64_t segs, int64_t slabs, int64_t streams,
+                                                                          float* __restrict__ ws, float* amax,
+                                                                          const float* __restrict__ scale2,
+                                                                          int force_exact) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
+  __shared__ CodeTables t;
+  __shared__ int32_t tp[128];
+  FqState q;
+  q.t = &t;
+  q.tp = tp;
+  q.s2 = *scale2;
+  q.inv = (float)(1.0 / (6.0 * (double)q.s2));
+  q.est = q.inv > 0.0f && q.inv < __builtin_inff();
+  build_code_search(tp, q.s2);
+  build_code_tables(t, q.s2, force_exact);                 // syncs
+  const int mode = table_mode(t);
+  u16x2 amx;
+  if (mode == 0)
+    amx = partial_body<0>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
+  else if (mode == 1)
+    amx = partial_body<1>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
+  else
+    amx = partial_body<2>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
+  if (amax) reduce_amax(amx, amax);
 }
 
 // H[g] += sum of the partials of group g over the workgroups whose range
@@ -329,22 +388,16 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __res
 
 }  // namespace
 
+static size_t plan_bytes(const Plan& p) { return (size_t)(p.wgs * p.segs) * kSlabGroups * 256u * sizeof(float); }
+
+// one query for both variants: the larger of their partial buffers
 size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
-  const Plan p = plan(tokens, k);
-  return (size_t)(p.wgs * p.segs) * kSlabGroups * 256u * sizeof(float);
+  const size_t a = plan_bytes(plan(tokens, k, kTargetWgs));
+  const size_t b = plan_bytes(plan(tokens, k, kTargetWgsFq));
+  return a > b ? a : b;
 }
 
-template <bool FQ>
-static int launch_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
-                        float* amax, void* workspace, hipStream_t s) {
-  const Plan p = plan(tokens, k);
-  if (p.wgs == 0) return NVFP4_OK;
-  float* ws = static_cast<float*>(workspace);
-  hessian_partial_kernel<FQ><<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs,
-                                                                    p.segs, p.slabs, p.streams, ws, amax, scale2,
-                                                                    FQ ? force_exact_flag() : 0);
-  int st = launch_status("hessian_partial_kernel");
-  if (st) return st;
+static int launch_reduce(const Plan& p, int64_t k, const float* ws, float* H, hipStream_t s) {
   hessian_reduce_kernel<<<(unsigned)(k / 16), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles, p.total,
                                                             p.wgs, p.segs, reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
@@ -352,12 +405,25 @@ static int launch_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
 
 int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
                          void* workspace, hipStream_t s) {
-  return launch_accum<false>(x, tokens, k, ldx, nullptr, H, amax, workspace, s);
+  const Plan p = plan(tokens, k, kTargetWgs);
+  if (p.wgs == 0) return NVFP4_OK;
+  float* ws = static_cast<float*>(workspace);
+  hessian_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
+                                                               p.slabs, p.streams, ws, amax);
+  int st = launch_status("hessian_partial_kernel");
+  return st ? st : launch_reduce(p, k, ws, H, s);
 }
 
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
                             float* amax, void* workspace, hipStream_t s) {
-  return launch_accum<true>(x, tokens, k, ldx, scale2, H, amax, workspace, s);
+  const Plan p = plan(tokens, k, kTargetWgsFq);
+  if (p.wgs == 0) return NVFP4_OK;
+  float* ws = static_cast<float*>(workspace);
+  hessian_fq_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
+                                                                  p.slabs, p.streams, ws, amax, scale2,
+                                                                  force_exact_flag());
+  int st = launch_status("hessian_fq_partial_kernel");
+  return st ? st : launch_reduce(p, k, ws, H, s);
 }
 
 }  // namespace nvfp4

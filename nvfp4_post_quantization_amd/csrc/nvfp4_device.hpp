@@ -340,21 +340,20 @@ __device__ inline void build_code_search(int32_t* tp, float s2) {
 // rounding (computed on the bits) is at most one code off, and one compare on
 // each side against the exact thresholds fixes it.
 __device__ __forceinline__ int block_code_est(uint32_t P, const int32_t* tp, float inv) {
+  // written without branches so that several blocks' table reads can overlap
   const float y = __uint_as_float(P << 16) * inv;
-  int c;
-  if (y >= 0x1p-6f) {                                          // normal E4M3: 3 mantissa bits, RNE
-    const uint32_t b = __float_as_uint(y);
-    c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127 - 7) << 3);
-  } else {                                                     // subnormal E4M3: multiples of 2^-9
-    c = (int)rintf(y * 512.0f);
-  }
+  const uint32_t b = __float_as_uint(y);
+  const int cn = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127 - 7) << 3);   // normal E4M3: 3 bits, RNE
+  const int cs = (int)rintf(y * 512.0f);                                              // subnormal: k * 2^-9
+  int c = y >= 0x1p-6f ? cn : cs;
   c = min(max(c, 0), kCodes - 1);
+  // For c = 0 the lower threshold is tp[0] instead of "none": a decrement to
+  // -1 then only happens for P <= tp[0], where the answer is 0 (P = 0) or 1,
+  // which the final max gives.
   const int32_t hi = tp[c];
-  const int32_t lo = c > 0 ? tp[c - 1] : -1;
-  if ((int32_t)P > hi) ++c;
-  else if ((int32_t)P <= lo) --c;
-  if (c == 0 && P) c = 1;                                      // nonzero block: never scale 0
-  return c;
+  const int32_t lo = tp[max(c - 1, 0)];
+  c += ((int32_t)P > hi) - ((int32_t)P <= lo);                 // thresholds increase: at most one holds
+  return max(c, P ? 1 : 0);                                    // nonzero block: never scale 0
 }
 
 __device__ __forceinline__ int block_code(uint32_t P, const int32_t* tp, float s2) {
