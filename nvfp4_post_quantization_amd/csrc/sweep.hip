@@ -53,6 +53,14 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kPruneMargin = 2e-5f;
 
+// Value of v in lane src (a constant), broadcast through scalar registers.
+__device__ __forceinline__ double bcast(double v, int src) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // sqrt(S_i) of the wave's group, S_i = (1 - 1e-5) / (H^-1)_ii in fp64, H taken
 // from its upper triangle (as the cost is); all zero when H is not safely positive definite.
 // Lanes 0..15 own rows 0..15 (higher lanes duplicate them).  Writes out[0..15].
@@ -65,7 +73,7 @@ __device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
   double pmax = 0.0, pmin = 1e300;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const double pj = __shfl(a[j], j);              // updated A_jj from lane j
+    const double pj = bcast(a[j], j);               // updated A_jj from lane j
     ok = ok && (pj > 0.0);
     pmax = fmax(pmax, pj);
     pmin = fmin(pmin, pj);
@@ -74,7 +82,7 @@ __device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
     a[j] = lij;
 #pragma unroll
     for (int kk = j + 1; kk < 16; ++kk) {
-      const double lkj = __shfl(lij, kk);
+      const double lkj = bcast(lij, kk);
       if (i >= kk) a[kk] -= lij * lkj;
     }
   }
@@ -85,8 +93,8 @@ __device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
   for (int kk = 0; kk < 16; ++kk) {
     double acc = (kk == i) ? 1.0 : 0.0;
 #pragma unroll
-    for (int m = 0; m < kk; ++m) acc -= __shfl(a[m], kk) * y[m];
-    y[kk] = acc / __shfl(a[kk], kk);
+    for (int m = 0; m < kk; ++m) acc -= bcast(a[m], kk) * y[m];
+    y[kk] = acc / bcast(a[kk], kk);
     s += y[kk] * y[kk];
   }
   ok = ok && (pmin > 1e-9 * pmax) && (s > 0.0);
