@@ -25,15 +25,18 @@ Sources (page title, section):
   scale bytes double.
 * "FP4量化技术概述" (FP4 survey), §1.1 (E2M1 value set), §1.2 (block sizes,
   bits per element).
+* "Coder390 NVFP4 校正（校准）方式" §3 (layer table of the W4A4+W8A8 tier):
+  FP8 E4M3 weights and activations with static per-tensor scales (fp8.py).
 
 Readings where the pages are silent are marked "reading:" in the docstrings.
 
 Parity unpinned (readings the pages cannot confirm; no worked example is
 printed): the argmin tie-break (lowest code), the sign of a zero nibble, the
 exact-quotient rounding rule, nibble order within a byte, the clamp of a
-nonzero block's code to 0x01, the synthetic input recipes, and (for the W4A4
+nonzero block's code to 0x01, the synthetic input recipes, (for the W4A4
 Hessian variant) that the layer input is taken after its activation
-quantizer.
+quantizer, and (FP8 tier) the static scale amax/448 and the exact-quotient
+encode.
 """
 from .formats import (
     E2M1_MAGNITUDES, E4M3_VALUES, e2m1_decode, e2m1_encode, e4m3_value,
@@ -45,6 +48,7 @@ from .nvfp4 import (
     sweep_costs, scale_sweep, max_code, quantize_dynamic, dequant, hessian_fakequant,
 )
 from .mxcast import mxfp4_to_nvfp4, mxfp4_dequant
+from .fp8 import fp8_tensor_scale, fp8_quantize, fp8_dequant
 
 __all__ = [
     "E2M1_MAGNITUDES", "E4M3_VALUES", "e2m1_decode", "e2m1_encode", "e4m3_value",
@@ -53,4 +57,5 @@ __all__ = [
     "tensor_scale", "hessian", "block_scale", "quantize_at_code", "block_cost",
     "sweep_costs", "scale_sweep", "max_code", "quantize_dynamic", "dequant", "hessian_fakequant",
     "mxfp4_to_nvfp4", "mxfp4_dequant",
+    "fp8_tensor_scale", "fp8_quantize", "fp8_dequant",
 ]
