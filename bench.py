@@ -13,9 +13,10 @@ inputs:
   * activations X [8192, 4096]: a1 amax, a4 dynamic NVFP4 quantization and
     a5 the dequant round trip;
   * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast.
-After the timed steps, the W4A4 form of a2 (Hessian of the fake-quantized
-calibration streams) is timed on its own and reported under
-stages.next_w4a4_hessian; it is not part of the step.
+After the timed steps, two neighbouring pieces are timed on their own and
+reported under stages (not part of the step): the W4A4 form of a2 (Hessian
+of the fake-quantized calibration streams, next_w4a4_hessian) and the FP8
+E4M3 per-tensor static tier on the C3 activations (next_fp8_static).
 
 The headline value is weight blocks swept per second of whole-step time.
 Per-stage times come from HIP events on the stream the library launches on.
@@ -258,6 +259,36 @@ def main():
         "algorithmic_GB": round(x_bytes / 1e9, 4), "GBps": round(fq_gbs, 1),
         "frac_hbm_peak": round(fq_gbs / HBM_PEAK_GBS, 4),
         "kernel": "hessian_fq_partial_kernel+hessian_reduce_kernel"}
+
+    # FP8 E4M3 per-tensor static tier, outside the step: scale, quantize and
+    # dequant of the C3 activations [8192, 4096]
+    s8, am8 = torch.zeros(1, **f32), torch.zeros(1, **f32)
+    q8 = torch.empty((8192, 4096), **u8)
+    dq8 = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
+    ev8 = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def fp8_pass(ev):
+        ev[0].record(stream)
+        chk("fp8 scale", lib.fp8e4m3_compute_scale(x3.data_ptr(), x3.numel(), s8.data_ptr(), am8.data_ptr(), sptr))
+        ev[1].record(stream)
+        chk("fp8 quantize", lib.fp8e4m3_quantize(x3.data_ptr(), 8192, 4096, 4096, s8.data_ptr(), q8.data_ptr(), sptr))
+        ev[2].record(stream)
+        chk("fp8 dequant", lib.fp8e4m3_dequant(q8.data_ptr(), s8.data_ptr(), 8192, 4096, dq8.data_ptr(), sptr))
+        ev[3].record(stream)
+
+    fp8_pass(ev8)
+    t8 = [0.0, 0.0, 0.0]
+    for _ in range(args.steps):
+        fp8_pass(ev8)
+        torch.cuda.synchronize()
+        for i in range(3):
+            t8[i] += ev8[i].elapsed_time(ev8[i + 1]) / args.steps
+    e8 = x3.numel()
+    stage_rep["next_fp8_static"] = {"outside_step": True, "workload": "X [8192, 4096] bf16"}
+    for name, ms, nbytes in (("scale", t8[0], 2 * e8), ("quantize", t8[1], 3 * e8), ("dequant", t8[2], 3 * e8)):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        stage_rep["next_fp8_static"][name] = {"ms": round(ms, 4), "algorithmic_GB": round(nbytes / 1e9, 4),
+                                              "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
     if args.copy_probe:
         # an elementwise kernel of known traffic (4 GiB read + 4 GiB written per

@@ -222,6 +222,48 @@ int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups,
                         uint8_t* codes_out, float* scale2_out,
                         int64_t* fallback_blocks_out, void* stream);
 
+/*
+ * FP8 E4M3 tier with per-tensor static scales: the W8A8 layers of the mixed
+ * W4A4+W8A8 tier ("Coder390 NVFP4 校正（校准）方式" §3, layer table: attention
+ * projections in FP8 E4M3, activations with static scales from calibration).
+ * The page gives no formula; the scale is max calibration over the E4M3 range
+ * (the NVFP4 tensor scale of "NVFP4 量化流程说明" §3.4 without the E2M1
+ * factor 6) and the encode rounds the exact quotient like every encode here.
+ */
+
+/*
+ * s = RN_f32(amax / 448), amax = max |x| over n bf16 values.
+ * x [n] bf16, contiguous, 16-byte aligned (n may be 0: s = 0).
+ * scale_out device float[1] (also the running accumulator: must not alias x);
+ * amax_out device float[1] or NULL.
+ * Errors: NULL_ARG (x with n > 0, scale_out), BAD_SHAPE (n < 0), MISALIGNED, HIP.
+ */
+int fp8e4m3_compute_scale(const uint16_t* x, int64_t n, float* scale_out,
+                          float* amax_out, void* stream);
+
+/*
+ * q[r][c] = E4M3FN code of x[r][c] / s: the exact quotient rounded to nearest
+ * with ties to even, saturated at 448, sign in bit 7 (a negative value that
+ * rounds to zero gives 0x80).  s = 0 maps 0 to 0 and any other value to
+ * +-448.  Inputs are taken as finite.
+ * x     [rows][ldx] bf16, columns 0..k-1; rows 16-byte aligned (ldx % 8 == 0).
+ * scale device float[1], s >= 0 (e.g. from fp8e4m3_compute_scale).
+ * q     [rows][k] uint8, contiguous, 8-byte aligned.
+ * Errors: NULL_ARG, BAD_SHAPE (rows < 0, k <= 0, k % 8, ldx < k, overflow),
+ *         MISALIGNED, HIP.
+ */
+int fp8e4m3_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                     const float* scale, uint8_t* q, void* stream);
+
+/*
+ * out[r][c] = RN_bf16(RN_f32(e4m3(q[r][c]) * s)); codes 0x7F/0xFF give NaN.
+ * q [rows][k] uint8, contiguous, 8-byte aligned; out [rows][k] bf16,
+ * contiguous, 16-byte aligned.
+ * Errors: NULL_ARG, BAD_SHAPE (k % 8 and as above), MISALIGNED, HIP.
+ */
+int fp8e4m3_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t k,
+                    uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
     "hessian_accum", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
+    "fp8_compute_scale", "fp8_quantize", "fp8_dequant",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
@@ -44,6 +45,9 @@ _SIGS = {
     "nvfp4_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
     "mxfp4_to_nvfp4_cast": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p,
                                            _c_void_p, _c_void_p]),
+    "fp8e4m3_compute_scale": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "fp8e4m3_quantize": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "fp8e4m3_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -251,3 +255,43 @@ def mxfp4_to_nvfp4_cast(packed: torch.Tensor, e8m0: torch.Tensor, want_fallback:
         packed.data_ptr(), e8m0.data_ptr(), g, m, r, k, codes.data_ptr(), s2.data_ptr(),
         fb.data_ptr() if fb is not None else None, _stream(packed)))
     return codes, s2, fb
+
+
+def fp8_compute_scale(x: torch.Tensor, out=None):
+    """(s, amax) as float32[1] device tensors: s = RN_f32(amax/448) of bf16 x."""
+    _dev(x, torch.bfloat16, "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if out is None:
+        s = torch.empty(1, dtype=torch.float32, device=x.device)
+        am = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        s, am = out
+    _check("fp8e4m3_compute_scale", load().fp8e4m3_compute_scale(x.data_ptr(), x.numel(), s.data_ptr(),
+                                                                  am.data_ptr(), _stream(x)))
+    return s, am
+
+
+def fp8_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3FN codes uint8 [rows, k] of bf16 x [rows, k] / scale (per-tensor, static)."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(scale, torch.float32, "scale")
+    rows, k = x.shape
+    ldx = _row_major(x, "x")
+    q = torch.empty((rows, k), dtype=torch.uint8, device=x.device) if out is None else out
+    _check("fp8e4m3_quantize", load().fp8e4m3_quantize(x.data_ptr(), rows, k, ldx, scale.data_ptr(),
+                                                        q.data_ptr(), _stream(x)))
+    return q
+
+
+def fp8_dequant(q: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [rows, k] = RN_bf16(RN_f32(e4m3(q) * scale))."""
+    _dev(q, torch.uint8, "q", 2)
+    _dev(scale, torch.float32, "scale")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    rows, k = q.shape
+    o = torch.empty((rows, k), dtype=torch.bfloat16, device=q.device) if out is None else out
+    _check("fp8e4m3_dequant", load().fp8e4m3_dequant(q.data_ptr(), scale.data_ptr(), rows, k, o.data_ptr(),
+                                                      _stream(q)))
+    return o

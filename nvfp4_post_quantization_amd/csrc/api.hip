@@ -149,4 +149,33 @@ int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, in
                         fallback_blocks_out, as_stream(stream));
 }
 
+int fp8e4m3_compute_scale(const uint16_t* x, int64_t n, float* scale_out, float* amax_out, void* stream) {
+  if (n < 0 || !mul_fits(n, 2)) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale_out || (n > 0 && !x)) return NVFP4_ERR_NULL_ARG;
+  if (n > 0 && !aligned16(x)) return NVFP4_ERR_MISALIGNED;
+  return launch_fp8_scale(x, n, scale_out, amax_out, as_stream(stream));
+}
+
+int fp8e4m3_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale, uint8_t* q,
+                     void* stream) {
+  int st = check_matrix(rows, k, ldx, 2);
+  if (st) return st;
+  if (k % 8) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale || ((!x || !q) && rows > 0)) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx))) return st;
+  if (reinterpret_cast<uintptr_t>(q) % 8) return NVFP4_ERR_MISALIGNED;
+  return launch_fp8_quantize(x, rows, k, ldx, scale, q, as_stream(stream));
+}
+
+int fp8e4m3_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t k, uint16_t* out, void* stream) {
+  int st = check_matrix(rows, k, k, 2);
+  if (st) return st;
+  if (k % 8) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale || ((!q || !out) && rows > 0)) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if (reinterpret_cast<uintptr_t>(q) % 8 || !aligned16(out)) return NVFP4_ERR_MISALIGNED;
+  return launch_fp8_dequant(q, scale, rows, k, out, as_stream(stream));
+}
+
 }  // extern "C"

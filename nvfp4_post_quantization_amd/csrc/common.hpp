@@ -41,6 +41,10 @@ int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t l
                          void* workspace, hipStream_t s);
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
                             float* amax, void* workspace, hipStream_t s);
+int launch_fp8_scale(const uint16_t* x, int64_t n, float* scale_out, float* amax_out, hipStream_t s);
+int launch_fp8_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale, uint8_t* q,
+                        hipStream_t s);
+int launch_fp8_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t k, uint16_t* out, hipStream_t s);
 int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
                        const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s);
 int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,

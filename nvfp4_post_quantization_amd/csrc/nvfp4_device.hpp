@@ -315,17 +315,20 @@ __device__ __forceinline__ float e2m1_mag(int idx) {
   return 0.5f * (float)twice;
 }
 
-// Thresholds of the block-code search: code c is passed iff the block-max
-// bf16 pattern P > tp[c], where tp[c] is the largest pattern that stays at or
-// below the E4M3 midpoint between codes c and c+1 (times 6 * scale_2), ties
-// going to the even code.
-__device__ inline void build_code_search(int32_t* tp, float s2) {
+// Thresholds of an E4M3 encode of bf16 magnitudes over a scale S > 0:
+// the code RNE_sat(|x| / S) is the number of thresholds passed, where |x|
+// with bf16 pattern P passes tp[c] iff P > tp[c], tp[c] being the largest
+// pattern that stays at or below the midpoint between codes c and c+1 (times
+// S), ties going to the even code.  mid * S is exact in double (a midpoint has
+// at most 5 significant bits, S at most 26).  tp[126] is a sentinel that no
+// pattern passes (saturation at 448).
+__device__ inline void build_e4m3_thresholds(int32_t* tp, double S) {
   int c = threadIdx.x;
   if (c < 128) {
     int32_t t = 0x7FFFFFFF;
     if (c < kCodes - 1) {
       double mid = 0.5 * ((double)e4m3_value(c) + (double)e4m3_value(c + 1));
-      double M = mid * 6.0 * (double)s2;                       // exact (<= 31 bits)
+      double M = mid * S;
       uint32_t b0 = bf16_floor_pattern(M);
       bool at = bf16_pattern_value(b0) == M;
       bool tie_up = ((c + 1) & 1) == 0;
@@ -335,32 +338,49 @@ __device__ inline void build_code_search(int32_t* tp, float s2) {
   }
 }
 
-// Same result as block_code, for 0 < inv = RN_f32(1 / (6 scale_2)) < inf: the
-// FP32 quotient P * inv is within 2^-23 relative of the exact one, so its E4M3
-// rounding (computed on the bits) is at most one code off, and one compare on
-// each side against the exact thresholds fixes it.
-__device__ __forceinline__ int block_code_est(uint32_t P, const int32_t* tp, float inv) {
-  // written without branches so that several blocks' table reads can overlap
+// Thresholds of the block-code search: the block code is the E4M3 encode of
+// the block max over 6 * scale_2 (exact in double).
+__device__ inline void build_code_search(int32_t* tp, float s2) { build_e4m3_thresholds(tp, 6.0 * (double)s2); }
+
+// E4M3 code estimate of pattern P over the thresholds' scale S, for
+// 0 < inv = RN_f32(1 / S) < inf: the FP32 quotient P * inv is within 2^-23
+// relative of the exact one, so its E4M3 rounding (computed on the bits) is
+// at most one code off, and one compare on each side against the exact
+// thresholds fixes it.  Written without branches so that several values'
+// table reads can overlap.  For c = 0 the lower threshold read is tp[0]
+// instead of "none", so the result is -1 where the exact code is 0 (P <=
+// tp[0]); callers clamp.
+__device__ __forceinline__ int e4m3_code_est_raw(uint32_t P, const int32_t* tp, float inv) {
   const float y = __uint_as_float(P << 16) * inv;
   const uint32_t b = __float_as_uint(y);
   const int cn = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127 - 7) << 3);   // normal E4M3: 3 bits, RNE
   const int cs = (int)rintf(y * 512.0f);                                              // subnormal: k * 2^-9
   int c = y >= 0x1p-6f ? cn : cs;
   c = min(max(c, 0), kCodes - 1);
-  // For c = 0 the lower threshold is tp[0] instead of "none": a decrement to
-  // -1 then only happens for P <= tp[0], where the answer is 0 (P = 0) or 1,
-  // which the final max gives.
   const int32_t hi = tp[c];
   const int32_t lo = tp[max(c - 1, 0)];
-  c += ((int32_t)P > hi) - ((int32_t)P <= lo);                 // thresholds increase: at most one holds
-  return max(c, P ? 1 : 0);                                    // nonzero block: never scale 0
+  return c + ((int32_t)P > hi) - ((int32_t)P <= lo);          // thresholds increase: at most one holds
 }
 
-__device__ __forceinline__ int block_code(uint32_t P, const int32_t* tp, float s2) {
+// Exact E4M3 code of pattern P by binary search over the thresholds (any S).
+__device__ __forceinline__ int e4m3_code_search(uint32_t P, const int32_t* tp) {
   int pos = 0;
 #pragma unroll
   for (int step = 64; step >= 1; step >>= 1)
     if (tp[pos + step - 1] < (int32_t)P) pos += step;
+  return pos;
+}
+
+// The dynamic quantizer's block code from the block-max pattern P (tables
+// from build_code_search): the E4M3 encode of P / (6 scale_2), for
+// 0 < inv = RN_f32(1 / (6 scale_2)) < inf.  A nonzero block never gets scale 0
+// (for c = 0 the raw estimate gives -1 or 0, both lifted by the final max).
+__device__ __forceinline__ int block_code_est(uint32_t P, const int32_t* tp, float inv) {
+  return max(e4m3_code_est_raw(P, tp, inv), P ? 1 : 0);
+}
+
+__device__ __forceinline__ int block_code(uint32_t P, const int32_t* tp, float s2) {
+  int pos = e4m3_code_search(P, tp);
   if (s2 == 0.0f) pos = P ? (kCodes - 1) : 0;
   if (pos == 0 && P) pos = 1;                                  // nonzero block: never scale 0
   return pos;

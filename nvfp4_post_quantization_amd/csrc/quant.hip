@@ -93,16 +93,19 @@ __global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __rest
   publish_max(m, acc);
 }
 
-__global__ void amax_finalize_kernel(const uint32_t* acc, float* scale2_out, float* amax_out) {
+// scale = amax / 6 / 448 (NVFP4 tensor scale) or amax / 448 (FP8 E4M3
+// per-tensor scale), in double and then stored as FP32.
+__global__ void amax_finalize_kernel(const uint32_t* acc, float* scale2_out, float* amax_out, int fp8) {
   if (threadIdx.x == 0) {
     float amax = __uint_as_float(*acc);
-    float s2 = (float)((double)amax / 6.0 / 448.0);
+    float s2 = fp8 ? (float)((double)amax / 448.0) : (float)((double)amax / 6.0 / 448.0);
     if (amax_out) *amax_out = amax;
     *scale2_out = s2;
   }
 }
 
-int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, hipStream_t s) {
+static int launch_amax_scale(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, int fp8,
+                             hipStream_t s) {
   uint32_t* acc = reinterpret_cast<uint32_t*>(amax_out ? amax_out : scale2_out);
   amax_init_kernel<<<1, 64, 0, s>>>(acc);
   int st = launch_status("amax_init_kernel");
@@ -115,8 +118,16 @@ int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float
     st = launch_status("amax_reduce_kernel");
     if (st) return st;
   }
-  amax_finalize_kernel<<<1, 64, 0, s>>>(acc, scale2_out, amax_out);
+  amax_finalize_kernel<<<1, 64, 0, s>>>(acc, scale2_out, amax_out, fp8);
   return launch_status("amax_finalize_kernel");
+}
+
+int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, hipStream_t s) {
+  return launch_amax_scale(x, n, scale2_out, amax_out, 0, s);
+}
+
+int launch_fp8_scale(const uint16_t* x, int64_t n, float* scale_out, float* amax_out, hipStream_t s) {
+  return launch_amax_scale(x, n, scale_out, amax_out, 1, s);
 }
 
 // ------------------------------------------------------ dynamic quantizer ----

@@ -37,7 +37,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
         "nvfp4_hessian_accum", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
-        "mxfp4_to_nvfp4_cast",
+        "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -135,3 +135,30 @@ def test_python_layer_rejects_cpu_tensors():
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         nq.quantize_dynamic(x, torch.zeros(1))
+
+
+def test_fp8_validation(lib):
+    cs = lib.fp8e4m3_compute_scale
+    assert cs(P, -1, P, None, None) == SHAPE
+    assert cs(None, 8, P, None, None) == NULL
+    assert cs(P, 8, None, None, None) == NULL
+    assert cs(P + 2, 8, P, None, None) == ALIGN
+    q = lib.fp8e4m3_quantize
+    assert q(P, 4, 12, 16, P, P, None) == SHAPE            # k % 8
+    assert q(P, 4, 16, 8, P, P, None) == SHAPE             # ld < k
+    assert q(P, -1, 16, 16, P, P, None) == SHAPE
+    assert q(P, 4, 16, 16, None, P, None) == NULL          # scale
+    assert q(None, 4, 16, 16, P, P, None) == NULL
+    assert q(P, 4, 16, 16, P, None, None) == NULL
+    assert q(P + 2, 4, 16, 16, P, P, None) == ALIGN
+    assert q(P, 4, 16, 20, P, P, None) == ALIGN            # row stride not 16 B
+    assert q(P, 4, 16, 16, P, P + 4, None) == ALIGN        # q not 8-byte aligned
+    assert q(P, 0, 16, 16, P, None, None) == OK
+    assert q(P, 1 << 62, 16, 1 << 40, P, P, None) == SHAPE
+    d = lib.fp8e4m3_dequant
+    assert d(P, P, 4, 12, P, None) == SHAPE
+    assert d(P, None, 4, 16, P, None) == NULL
+    assert d(None, P, 4, 16, P, None) == NULL
+    assert d(P + 4, P, 4, 16, P, None) == ALIGN
+    assert d(P, P, 4, 16, P + 8, None) == ALIGN
+    assert d(None, P, 0, 16, None, None) == OK
