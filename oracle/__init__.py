@@ -27,6 +27,8 @@ Sources (page title, section):
   bits per element).
 * "Coder390 NVFP4 校正（校准）方式" §3 (layer table of the W4A4+W8A8 tier):
   FP8 E4M3 weights and activations with static per-tensor scales (fp8.py).
+* "FP4量化技术概述" §3.1 (MR-GPTQ): block Hadamard rotation fused into the
+  weights, W' = W H, activations rotated online (rotate.py).
 
 Readings where the pages are silent are marked "reading:" in the docstrings.
 
@@ -35,13 +37,14 @@ printed): the argmin tie-break (lowest code), the sign of a zero nibble, the
 exact-quotient rounding rule, nibble order within a byte, the clamp of a
 nonzero block's code to 0x01, the synthetic input recipes, (for the W4A4
 Hessian variant) that the layer input is taken after its activation
-quantizer, and (FP8 tier) the static scale amax/448 and the exact-quotient
-encode.
+quantizer, (FP8 tier) the static scale amax/448 and the exact-quotient
+encode, and (rotation) the per-group input-channel rotation, its butterfly
+order and the single rounding to bf16.
 """
 from .formats import (
     E2M1_MAGNITUDES, E4M3_VALUES, e2m1_decode, e2m1_encode, e4m3_value,
     e4m3_encode_ratio, e8m0_value, bf16_bits_to_f64, f64_to_bf16_bits, f32,
-    pack_nibbles, unpack_nibbles,
+    pack_nibbles, unpack_nibbles, f64_to_bf16_rne,
 )
 from .nvfp4 import (
     tensor_scale, hessian, block_scale, quantize_at_code, block_cost,
@@ -49,13 +52,15 @@ from .nvfp4 import (
 )
 from .mxcast import mxfp4_to_nvfp4, mxfp4_dequant
 from .fp8 import fp8_tensor_scale, fp8_quantize, fp8_dequant
+from .rotate import hadamard16, rotate_blocks, rotate_hessian
 
 __all__ = [
     "E2M1_MAGNITUDES", "E4M3_VALUES", "e2m1_decode", "e2m1_encode", "e4m3_value",
     "e4m3_encode_ratio", "e8m0_value", "bf16_bits_to_f64", "f64_to_bf16_bits", "f32",
-    "pack_nibbles", "unpack_nibbles",
+    "pack_nibbles", "unpack_nibbles", "f64_to_bf16_rne",
     "tensor_scale", "hessian", "block_scale", "quantize_at_code", "block_cost",
     "sweep_costs", "scale_sweep", "max_code", "quantize_dynamic", "dequant", "hessian_fakequant",
     "mxfp4_to_nvfp4", "mxfp4_dequant",
     "fp8_tensor_scale", "fp8_quantize", "fp8_dequant",
+    "hadamard16", "rotate_blocks", "rotate_hessian",
 ]

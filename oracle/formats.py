@@ -151,3 +151,23 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     r = (u.astype(np.uint64) + np.uint64(0x7FFF) + lsb.astype(np.uint64)) >> np.uint64(16)
     return r.astype(np.uint16)
+
+
+def f64_to_bf16_rne(x) -> np.ndarray:
+    """bf16 bit patterns of float64 values rounded ONCE to nearest, ties to
+    even (subnormals on the 2^-133 grid, overflow to infinity).
+
+    Unlike f64_to_bf16_bits this does not go through float32 first.  The grid
+    step at |x| in [2^e, 2^(e+1)) is 2^(max(e, -126) - 7); |x| divided by it
+    is exact, rint rounds half to even, and the product is exact again.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    m, ex = np.frexp(a)                              # a = m 2^ex, 0.5 <= m < 1
+    e = np.where(a > 0, ex - 1, -126)
+    q = np.ldexp(1.0, np.maximum(e, -126) - 7)
+    v = np.rint(a / q) * q
+    with np.errstate(over="ignore"):
+        u = v.astype(np.float32).view(np.uint32) >> np.uint32(16)   # exact; 2^128 and above -> inf
+    u = u | np.where(np.signbit(x), np.uint32(0x8000), np.uint32(0))
+    return u.astype(np.uint16)
