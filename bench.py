@@ -15,8 +15,10 @@ inputs:
   * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast.
 After the timed steps, two neighbouring pieces are timed on their own and
 reported under stages (not part of the step): the W4A4 form of a2 (Hessian
-of the fake-quantized calibration streams, next_w4a4_hessian) and the FP8
-E4M3 per-tensor static tier on the C3 activations (next_fp8_static).
+of the fake-quantized calibration streams, next_w4a4_hessian), the FP8 E4M3
+per-tensor static tier on the C3 activations (next_fp8_static), and the
+block-Hadamard rotation with the sweep under it and its cost against the
+plain sweep's (next_block_hadamard).
 
 The headline value is weight blocks swept per second of whole-step time.
 Per-stage times come from HIP events on the stream the library launches on.
@@ -289,6 +291,59 @@ def main():
         gbs = nbytes / (ms / 1e3) / 1e9
         stage_rep["next_fp8_static"][name] = {"ms": round(ms, 4), "algorithmic_GB": round(nbytes / 1e9, 4),
                                               "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    # Block-Hadamard rotation under the sweep, outside the step: W' = W R for
+    # the three weights, H' = R^T H R for both streams, then the sweep of
+    # (W', H') at scale_2(W'); its total cost is compared with the plain
+    # sweep's (both are the Hessian-weighted error in the original basis)
+    Wr = {n: torch.empty_like(w) for n, w in W.items()}
+    Hr = {s: torch.empty_like(H[s]) for s in (0, 1)}
+    s2r = {n: torch.zeros(1, **f32) for n in W}
+    cost_p = {n: torch.empty((w.shape[0], w.shape[1] // 16), **f32) for n, w in W.items()}
+    cost_r = {n: torch.empty((w.shape[0], w.shape[1] // 16), **f32) for n, w in W.items()}
+    evr = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def rot_pass(ev):
+        ev[0].record(stream)
+        for n, w in W.items():
+            chk("hadamard", lib.nvfp4_block_hadamard(w.data_ptr(), w.shape[0], w.shape[1], w.shape[1],
+                                                     Wr[n].data_ptr(), w.shape[1], sptr))
+        ev[1].record(stream)
+        for s in (0, 1):
+            chk("hessian hadamard", lib.nvfp4_hessian_hadamard(H[s].data_ptr(), H[s].shape[0], Hr[s].data_ptr(), sptr))
+        for n, w in W.items():
+            chk("scale2", lib.nvfp4_compute_scale2(Wr[n].data_ptr(), w.numel(), s2r[n].data_ptr(), None, sptr))
+        ev[2].record(stream)
+        for n, w in W.items():
+            p, c = sw_out[n]
+            chk("sweep", lib.nvfp4_scale_sweep(Wr[n].data_ptr(), w.shape[0], w.shape[1], w.shape[1],
+                                               Hr[hin[n]].data_ptr(), s2r[n].data_ptr(), p.data_ptr(),
+                                               c.data_ptr(), cost_r[n].data_ptr(), sptr))
+        ev[3].record(stream)
+
+    for n, w in W.items():                                      # plain sweep with costs, for the comparison
+        p, c = sw_out[n]
+        chk("sweep", lib.nvfp4_scale_sweep(w.data_ptr(), w.shape[0], w.shape[1], w.shape[1], H[hin[n]].data_ptr(),
+                                           s2w[n].data_ptr(), p.data_ptr(), c.data_ptr(), cost_p[n].data_ptr(), sptr))
+    rot_pass(evr)
+    tr = [0.0, 0.0, 0.0]
+    reps = max(1, min(args.steps, 3))
+    for _ in range(reps):
+        rot_pass(evr)
+        torch.cuda.synchronize()
+        for i in range(3):
+            tr[i] += evr[i].elapsed_time(evr[i + 1]) / reps
+    w_elems = sum(w.numel() for w in W.values())
+    rot_gbs = 4 * w_elems / (tr[0] / 1e3) / 1e9
+    stage_rep["next_block_hadamard"] = {
+        "outside_step": True,
+        "rotate_weights": {"ms": round(tr[0], 4), "launches": 3, "algorithmic_GB": round(4 * w_elems / 1e9, 4),
+                           "GBps": round(rot_gbs, 1), "frac_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4)},
+        "rotate_hessians_and_scale2_ms": round(tr[1], 4),
+        "rotated_sweep": {"ms": round(tr[2], 4), "blocks_per_s": round(blocks / (tr[2] / 1e3), 1)},
+        "total_cost_rotated_over_plain": {n: round(float(cost_r[n].double().sum() / cost_p[n].double().sum()), 5)
+                                          for n in W},
+    }
 
     if args.copy_probe:
         # an elementwise kernel of known traffic (4 GiB read + 4 GiB written per

@@ -264,6 +264,35 @@ int fp8e4m3_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
 int fp8e4m3_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t k,
                     uint16_t* out, void* stream);
 
+/*
+ * Block-Hadamard rotation of the input channels under the local-Hessian sweep
+ * ("FP4量化技术概述：从理论到硬件实现" §3.1, MR-GPTQ: the block Hadamard
+ * transform fused into the weights, W' = W H, activations rotated online).
+ * Per NVFP4 group of 16 input channels R_g = H16 / 4 (Sylvester order), so
+ * X W^T = (X R)(W R)^T; the rotated input's local Hessian is R_g^T H_g R_g,
+ * and the sweep of (W R, R^T H R) has the cost of the un-rotated error, so
+ * its costs compare directly with the plain sweep's.
+ */
+
+/*
+ * out[r][16g + i] = RN_bf16(((x[r][16g:16g+16] H16) / 4)_i): the Sylvester
+ * butterfly in fp64 (exact unless a block spans more than 2^41), rounded once
+ * to bf16 (nearest even).  Rotates weights (W R) and activations (X R) alike.
+ * x   [rows][ldx] bf16, columns 0..k-1; out [rows][ldo] bf16.  Rows 16-byte
+ *     aligned (ldx, ldo multiples of 8).  out may be x itself with ldo == ldx
+ *     (in place); otherwise the two must not overlap.
+ * Errors: NULL_ARG, BAD_SHAPE (k % 16, ld < k, sizes), MISALIGNED, HIP.
+ */
+int nvfp4_block_hadamard(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                         uint16_t* out, int64_t ldo, void* stream);
+
+/*
+ * H_out[g] = RN_f32(R_g^T H[g] R_g) for g < groups, in fp64.  H and H_out are
+ * [groups][16][16] float; H_out may be H (in place), otherwise no overlap.
+ * Errors: NULL_ARG, BAD_SHAPE (groups < 0), HIP.
+ */
+int nvfp4_hessian_hadamard(const float* H, int64_t groups, float* H_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

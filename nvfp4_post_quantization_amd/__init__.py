@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
     "hessian_accum", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
-    "fp8_compute_scale", "fp8_quantize", "fp8_dequant",
+    "fp8_compute_scale", "fp8_quantize", "fp8_dequant", "block_hadamard", "hessian_hadamard",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
@@ -48,6 +48,8 @@ _SIGS = {
     "fp8e4m3_compute_scale": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "fp8e4m3_quantize": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "fp8e4m3_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
+    "nvfp4_block_hadamard": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p]),
+    "nvfp4_hessian_hadamard": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -295,3 +297,30 @@ def fp8_dequant(q: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None =
     _check("fp8e4m3_dequant", load().fp8e4m3_dequant(q.data_ptr(), scale.data_ptr(), rows, k, o.data_ptr(),
                                                       _stream(q)))
     return o
+
+
+def block_hadamard(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 X R: each 16-element row block times H16 / 4 (fp64 butterfly, one
+    rounding).  out may be x itself (in place)."""
+    _dev(x, torch.bfloat16, "x", 2)
+    rows, k = x.shape
+    ldx = _row_major(x, "x")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out", 2)
+    ldo = _row_major(out, "out")
+    _check("nvfp4_block_hadamard", load().nvfp4_block_hadamard(x.data_ptr(), rows, k, ldx, out.data_ptr(), ldo,
+                                                                _stream(x)))
+    return out
+
+
+def hessian_hadamard(H: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """R^T H R per group of a float32 [groups, 16, 16] Hessian (out may be H)."""
+    _dev(H, torch.float32, "H")
+    if not H.is_contiguous() or H.numel() % 256:
+        raise ValueError("H must be a contiguous float32 [groups, 16, 16] tensor")
+    if out is None:
+        out = torch.empty_like(H)
+    _check("nvfp4_hessian_hadamard", load().nvfp4_hessian_hadamard(H.data_ptr(), H.numel() // 256,
+                                                                    out.data_ptr(), _stream(H)))
+    return out

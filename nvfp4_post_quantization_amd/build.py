@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4mi.so")
-SOURCES = ["api.hip", "quant.hip", "hessian.hip", "sweep.hip", "cast.hip", "fp8.hip"]
+SOURCES = ["api.hip", "quant.hip", "hessian.hip", "sweep.hip", "cast.hip", "fp8.hip", "rotate.hip"]
 ARCH = os.environ.get("NVFP4MI_ARCH", "gfx950")
 
 FLAGS = [

@@ -178,4 +178,23 @@ int fp8e4m3_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t 
   return launch_fp8_dequant(q, scale, rows, k, out, as_stream(stream));
 }
 
+int nvfp4_block_hadamard(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint16_t* out, int64_t ldo,
+                         void* stream) {
+  int st = check_matrix(rows, k, ldx, 2);
+  if (st) return st;
+  if ((st = check_matrix(rows, k, ldo, 2))) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if ((!x || !out) && rows > 0) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx)) || (st = check_bf16_rows(out, ldo))) return st;
+  return launch_block_hadamard(x, rows, k, ldx, out, ldo, as_stream(stream));
+}
+
+int nvfp4_hessian_hadamard(const float* H, int64_t groups, float* H_out, void* stream) {
+  if (groups < 0 || !mul_fits(groups, 1024)) return NVFP4_ERR_BAD_SHAPE;
+  if (groups == 0) return NVFP4_OK;
+  if (!H || !H_out) return NVFP4_ERR_NULL_ARG;
+  return launch_hessian_hadamard(H, groups, H_out, as_stream(stream));
+}
+
 }  // extern "C"

@@ -45,6 +45,9 @@ int launch_fp8_scale(const uint16_t* x, int64_t n, float* scale_out, float* amax
 int launch_fp8_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale, uint8_t* q,
                         hipStream_t s);
 int launch_fp8_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t k, uint16_t* out, hipStream_t s);
+int launch_block_hadamard(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint16_t* out, int64_t ldo,
+                          hipStream_t s);
+int launch_hessian_hadamard(const float* H, int64_t groups, float* Hout, hipStream_t s);
 int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
                        const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s);
 int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,

@@ -38,6 +38,7 @@ def test_header_symbols_exported(lib):
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
         "nvfp4_hessian_accum", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
+        "nvfp4_block_hadamard", "nvfp4_hessian_hadamard",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -162,3 +163,21 @@ def test_fp8_validation(lib):
     assert d(P + 4, P, 4, 16, P, None) == ALIGN
     assert d(P, P, 4, 16, P + 8, None) == ALIGN
     assert d(None, P, 0, 16, None, None) == OK
+
+
+def test_hadamard_validation(lib):
+    b = lib.nvfp4_block_hadamard
+    assert b(P, 4, 24, 24, P, 24, None) == SHAPE            # k % 16
+    assert b(P, 4, 32, 16, P, 32, None) == SHAPE            # ldx < k
+    assert b(P, 4, 32, 32, P, 16, None) == SHAPE            # ldo < k
+    assert b(None, 4, 32, 32, P, 32, None) == NULL
+    assert b(P, 4, 32, 32, None, 32, None) == NULL
+    assert b(P + 2, 4, 32, 32, P, 32, None) == ALIGN
+    assert b(P, 4, 32, 32, P + 2, 32, None) == ALIGN
+    assert b(P, 4, 32, 36, P, 32, None) == ALIGN
+    assert b(P, 0, 32, 32, None, 32, None) == OK
+    h = lib.nvfp4_hessian_hadamard
+    assert h(P, -1, P, None) == SHAPE
+    assert h(None, 4, P, None) == NULL
+    assert h(P, 4, None, None) == NULL
+    assert h(None, 0, None, None) == OK
