@@ -49,6 +49,7 @@ from .formats import (
 from .nvfp4 import (
     tensor_scale, hessian, block_scale, quantize_at_code, block_cost,
     sweep_costs, scale_sweep, max_code, quantize_dynamic, dequant, hessian_fakequant,
+    fakequant, quantlinear_forward,
 )
 from .mxcast import mxfp4_to_nvfp4, mxfp4_dequant
 from .fp8 import fp8_tensor_scale, fp8_quantize, fp8_dequant
@@ -60,6 +61,7 @@ __all__ = [
     "pack_nibbles", "unpack_nibbles", "f64_to_bf16_rne",
     "tensor_scale", "hessian", "block_scale", "quantize_at_code", "block_cost",
     "sweep_costs", "scale_sweep", "max_code", "quantize_dynamic", "dequant", "hessian_fakequant",
+    "fakequant", "quantlinear_forward",
     "mxfp4_to_nvfp4", "mxfp4_dequant",
     "fp8_tensor_scale", "fp8_quantize", "fp8_dequant",
     "hadamard16", "rotate_blocks", "rotate_hessian",

@@ -156,6 +156,26 @@ def dequant(packed, codes, s2):
     return f64_to_bf16_bits(f32(v).reshape(rows, k))
 
 
+def fakequant(x_bits, s2):
+    """bf16 bits of the NVFP4 block fake QDQ of an activation tensor: the
+    dynamic quantizer followed by the two-DQ chain (pi05 flow note §2.2: the
+    input quantizer of a QuantLinear; §3.4-§3.5, §5.4)."""
+    packed, codes = quantize_dynamic(x_bits, s2)
+    return dequant(packed, codes, s2)
+
+
+def quantlinear_forward(x_bits, s2x, w_hat_bits):
+    """Fake-quant QuantLinear forward (pi05 flow note §2.2, §2.4): x goes
+    through its input quantizer (fake QDQ at tensor scale s2x), the weight is
+    already fake-quantized (w_hat = dequant of the swept NVFP4 weight), and
+    y = x_hat w_hat^T is a floating-point matmul.  Returned in float64,
+    unrounded (reading: the GEMM accumulates in fp32 and rounds y once to
+    bf16; that rounding and the accumulation order are left to the tests'
+    error bound)."""
+    xh = bf16_bits_to_f64(fakequant(x_bits, s2x))
+    return xh @ bf16_bits_to_f64(w_hat_bits).T
+
+
 def hessian_fakequant(x_bits, s2, h_init=None):
     """Step 2 for a W4A4 calibration (reading: the layer input is seen after
     its dynamic NVFP4 quantizer): H_g += Xh_g^T Xh_g with Xh the bf16 output

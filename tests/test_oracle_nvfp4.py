@@ -275,3 +275,49 @@ def test_hessian_fakequant_identity_and_zero():
     assert not np.array_equal(hf, N.hessian(y))
     assert np.array_equal(hf, hf.transpose(0, 2, 1))
     assert np.min(np.linalg.eigvalsh(hf)) >= -1e-9 * np.max(np.abs(hf))
+
+
+def test_fakequant_identity_bound_and_zero_scale():
+    """Fake QDQ of an activation: identity on values the quantizer reproduces,
+    error at most half a step d/2 per element below saturation, all zero at
+    scale_2 = 0."""
+    rng = np.random.default_rng(41)
+    s2 = 2.0 ** -9
+    rows = []
+    for _ in range(24):
+        code = int(rng.integers(16, 110))
+        d = float(F.E4M3_VALUES[code]) * s2
+        q = rng.choice(F.E2M1_MAGNITUDES, 32) * rng.choice([-1.0, 1.0], 32)
+        q[3], q[20] = -6.0, 6.0
+        rows.append(q * d)
+    x = datagen.f32_to_bf16_bits(np.array(rows).astype(np.float32))
+    assert np.array_equal(N.fakequant(x, s2), x)
+    y = datagen.config1()[1]
+    _, s2y = N.tensor_scale(y)
+    yv = F.bf16_bits_to_f64(y).reshape(-1, 16)
+    fq = F.bf16_bits_to_f64(N.fakequant(y, s2y)).reshape(-1, 16)
+    d = N.block_scale(N.max_code(np.max(np.abs(yv), axis=1), s2y), s2y)[:, None]
+    # E2M1 spacing is at most 2 d below 6 d: the error is at most d, plus the bf16 rounding
+    assert np.all(np.abs(fq - yv) <= d * (1 + 2.0 ** -7) + 2.0 ** -8 * np.abs(yv))
+    assert not np.any(F.bf16_bits_to_f64(N.fakequant(y, 0.0)))
+
+
+def test_quantlinear_forward_equals_integer_matmul():
+    """With inputs the quantizers reproduce exactly (small integers times a
+    power of two, block max 6 d), the forward is an exact integer matmul."""
+    rng = np.random.default_rng(42)
+    s2 = 2.0 ** -10
+    code = 0x48                          # e4m3 value 16 -> d = 2^-6; every block holds E2M1 levels times d
+    d = float(F.E4M3_VALUES[code]) * s2
+    lv = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    xi = rng.integers(0, 8, (40, 64)); xs = rng.choice([-1, 1], (40, 64))
+    xi[:, ::16] = 7                      # block max 6 d: the block keeps code 0x48
+    x_val = xs * lv[xi] * d
+    x = datagen.f32_to_bf16_bits(x_val.astype(np.float32))
+    w_int = rng.integers(-8, 9, (24, 64))
+    w = datagen.f32_to_bf16_bits((w_int * 2.0 ** -5).astype(np.float32))
+    y = N.quantlinear_forward(x, s2, w)
+    # exact: x = (2 * xs * lv) * d / 2 with 2*lv integer; y = sum x w
+    xi2 = (xs * (2 * lv[xi])).astype(np.int64)
+    y_int = xi2 @ w_int.T                # in units of d/2 * 2^-5
+    assert np.array_equal(y, y_int * (d / 2) * 2.0 ** -5)
