@@ -16,9 +16,11 @@ inputs:
 After the timed steps, two neighbouring pieces are timed on their own and
 reported under stages (not part of the step): the W4A4 form of a2 (Hessian
 of the fake-quantized calibration streams, next_w4a4_hessian), the FP8 E4M3
-per-tensor static tier on the C3 activations (next_fp8_static), and the
+per-tensor static tier on the C3 activations (next_fp8_static), the
 block-Hadamard rotation with the sweep under it and its cost against the
-plain sweep's (next_block_hadamard).
+plain sweep's (next_block_hadamard), and the fake-quant QuantLinear forward
+of one calibration chunk through the swept gate weight
+(next_quantlinear_forward).
 
 The headline value is weight blocks swept per second of whole-step time.
 Per-stage times come from HIP events on the stream the library launches on.
@@ -42,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, spec
 FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 matrix (and packed vector), spec
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, spec
 SWEEP_FLOP_PER_BLOCK = 127 * (304 + 64)      # minimal method work per 16-element block
 C5_FALLBACK_BYTES = 32           # a fallback MX block reads and writes 16 bytes of nibbles
 
@@ -344,6 +347,56 @@ def main():
         "total_cost_rotated_over_plain": {n: round(float(cost_r[n].double().sum() / cost_p[n].double().sum()), 5)
                                           for n in W},
     }
+
+    # Fake-quant QuantLinear forward, outside the step: one 65536-token chunk
+    # [65536, 4096] through the gate weight after the sweep (w_hat = two-DQ of
+    # the swept NVFP4 weight, [12288, 4096]); the activation's scale_2 from max
+    # calibration of that chunk
+    xq = X[0][0]
+    wq_hat = torch.empty_like(W["gate"])
+    p, c = sw_out["gate"]
+    chk("dequant", lib.nvfp4_dequant(p.data_ptr(), c.data_ptr(), s2w["gate"].data_ptr(), W["gate"].shape[0],
+                                     W["gate"].shape[1], wq_hat.data_ptr(), sptr))
+    s2q = torch.zeros(1, **f32)
+    chk("scale2", lib.nvfp4_compute_scale2(xq.data_ptr(), xq.numel(), s2q.data_ptr(), None, sptr))
+    tq, kq, oq = xq.shape[0], xq.shape[1], wq_hat.shape[0]
+    yq = torch.empty((tq, oq), dtype=torch.bfloat16, device=dev)
+    wsq = torch.empty(lib.nvfp4_quantlinear_workspace_bytes(tq, kq), **u8)
+    xhq = torch.empty_like(xq)
+    evq = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+
+    def ql_pass(ev):
+        ev[0].record(stream)
+        chk("fakequant", lib.nvfp4_fakequant(xq.data_ptr(), tq, kq, kq, s2q.data_ptr(), xhq.data_ptr(), kq, sptr))
+        ev[1].record(stream)
+        chk("forward", lib.nvfp4_quantlinear_forward(xq.data_ptr(), tq, kq, kq, s2q.data_ptr(), wq_hat.data_ptr(),
+                                                     oq, kq, yq.data_ptr(), oq, wsq.data_ptr(), wsq.numel(), sptr))
+        ev[2].record(stream)
+        torch.matmul(xhq, wq_hat.t(), out=yq)                  # torch's GEMM on the same operands, for context
+        ev[3].record(stream)
+
+    ql_pass(evq)
+    tq_ms = [0.0, 0.0, 0.0]
+    reps = max(1, min(args.steps, 5))
+    for _ in range(reps):
+        ql_pass(evq)
+        torch.cuda.synchronize()
+        for i in range(3):
+            tq_ms[i] += evq[i].elapsed_time(evq[i + 1]) / reps
+    flop = 2.0 * tq * kq * oq
+    fq_b = 4.0 * tq * kq
+    stage_rep["next_quantlinear_forward"] = {
+        "outside_step": True,
+        "workload": f"x [{tq}, {kq}] bf16 through w_hat [{oq}, {kq}] (C4 gate, swept then dequantized)",
+        "fakequant": {"ms": round(tq_ms[0], 4), "algorithmic_GB": round(fq_b / 1e9, 4),
+                      "GBps": round(fq_b / (tq_ms[0] / 1e3) / 1e9, 1),
+                      "frac_hbm_peak": round(fq_b / (tq_ms[0] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "forward": {"ms": round(tq_ms[1], 4), "TFLOPs": round(flop / (tq_ms[1] / 1e3) / 1e12, 1),
+                    "frac_bf16_peak": round(flop / (tq_ms[1] / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "torch_matmul_same_operands": {"ms": round(tq_ms[2], 4),
+                                       "TFLOPs": round(flop / (tq_ms[2] / 1e3) / 1e12, 1)},
+    }
+    del yq, wsq, xhq
 
     if args.copy_probe:
         # an elementwise kernel of known traffic (4 GiB read + 4 GiB written per

@@ -293,6 +293,45 @@ int nvfp4_block_hadamard(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx
  */
 int nvfp4_hessian_hadamard(const float* H, int64_t groups, float* H_out, void* stream);
 
+/*
+ * NVFP4 block fake QDQ of an activation tensor, the QuantLinear input
+ * quantizer of "NVFP4 量化流程说明" §2.2: out = the bf16 result of
+ * nvfp4_dequant(nvfp4_quantize_dynamic(x, scale2)) element for element, in one
+ * pass without the packed intermediate.
+ * x [rows][ldx] bf16 and out [rows][ldo] bf16, columns 0..k-1, rows 16-byte
+ * aligned; scale2 device float[1].
+ * Errors: NULL_ARG, BAD_SHAPE (k % 16, ld < k, sizes), MISALIGNED, HIP.
+ */
+int nvfp4_fakequant(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                    const float* scale2, uint16_t* out, int64_t ldo, void* stream);
+
+/*
+ * Bytes of workspace nvfp4_quantlinear_forward needs (0 for invalid sizes).
+ */
+size_t nvfp4_quantlinear_workspace_bytes(int64_t tokens, int64_t k);
+
+/*
+ * Fake-quant QuantLinear forward of the calibration pass ("NVFP4 量化流程说明"
+ * §2.2, §2.4: x -> input quantizer (block fake QDQ) -> matmul with the
+ * fake-quantized weight, still a bf16 GEMM):
+ *   y[t][o] = RN_bf16( sum_k xh[t][k] w[o][k] ), fp32 accumulation,
+ * xh = nvfp4_fakequant(x, x_scale2).  w is the fake-quantized weight in bf16
+ * (nvfp4_dequant of the swept NVFP4 weight, computed once per layer).  The
+ * fake QDQ is one kernel of this library into the workspace; the product is
+ * a plain bf16 GEMM through hipBLASLt (fp32 compute; its summation order is
+ * hipBLASLt's).  The first call on a device creates a hipBLASLt handle (kept
+ * until the process ends); each new shape runs one algorithm query.
+ * x [tokens][ldx] bf16; w [out_features][ldw] bf16; y [tokens][ldy] bf16;
+ * rows 16-byte aligned.  workspace: 256-byte aligned device buffer of at
+ * least nvfp4_quantlinear_workspace_bytes(tokens, k) bytes (scratch).
+ * Errors: NULL_ARG, BAD_SHAPE (k % 16, ld < k, out_features <= 0, sizes),
+ *         MISALIGNED, WORKSPACE, HIP (also hipBLASLt failures).
+ */
+int nvfp4_quantlinear_forward(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
+                              const float* x_scale2, const uint16_t* w, int64_t out_features,
+                              int64_t ldw, uint16_t* y, int64_t ldy, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

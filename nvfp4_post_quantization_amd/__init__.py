@@ -24,6 +24,7 @@ __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
     "hessian_accum", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
     "fp8_compute_scale", "fp8_quantize", "fp8_dequant", "block_hadamard", "hessian_hadamard",
+    "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
@@ -50,6 +51,10 @@ _SIGS = {
     "fp8e4m3_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
     "nvfp4_block_hadamard": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p]),
     "nvfp4_hessian_hadamard": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p]),
+    "nvfp4_fakequant": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i64, _c_void_p]),
+    "nvfp4_quantlinear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "nvfp4_quantlinear_forward": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64,
+                                                 _c_void_p, _i64, _c_void_p, ctypes.c_size_t, _c_void_p]),
 }
 
 _lib = None
@@ -323,4 +328,46 @@ def hessian_hadamard(H: torch.Tensor, out: torch.Tensor | None = None) -> torch.
         out = torch.empty_like(H)
     _check("nvfp4_hessian_hadamard", load().nvfp4_hessian_hadamard(H.data_ptr(), H.numel() // 256,
                                                                     out.data_ptr(), _stream(H)))
+    return out
+
+
+def fakequant(x: torch.Tensor, scale2: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 NVFP4 block fake QDQ of x [rows, k] at tensor scale scale2 (f32[1])."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(scale2, torch.float32, "scale2")
+    rows, k = x.shape
+    ldx = _row_major(x, "x")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.bfloat16, device=x.device)
+    ldo = _row_major(out, "out")
+    _check("nvfp4_fakequant", load().nvfp4_fakequant(x.data_ptr(), rows, k, ldx, scale2.data_ptr(), out.data_ptr(),
+                                                      ldo, _stream(x)))
+    return out
+
+
+def quantlinear_workspace_bytes(tokens: int, k: int) -> int:
+    return int(load().nvfp4_quantlinear_workspace_bytes(tokens, k))
+
+
+def quantlinear_forward(x: torch.Tensor, x_scale2: torch.Tensor, w_hat: torch.Tensor,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y [tokens, out] = fakequant(x) @ w_hat^T (bf16 GEMM, fp32 accumulate);
+    w_hat is the fake-quantized weight [out, k] (nvfp4 dequant of the swept weight)."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(w_hat, torch.bfloat16, "w_hat", 2)
+    _dev(x_scale2, torch.float32, "x_scale2")
+    tokens, k = x.shape
+    o = w_hat.shape[0]
+    if w_hat.shape[1] != k:
+        raise ValueError("w_hat must be [out_features, k]")
+    ldx, ldw = _row_major(x, "x"), _row_major(w_hat, "w_hat")
+    if out is None:
+        out = torch.empty((tokens, o), dtype=torch.bfloat16, device=x.device)
+    ldy = _row_major(out, "out")
+    need = quantlinear_workspace_bytes(tokens, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("nvfp4_quantlinear_forward", load().nvfp4_quantlinear_forward(
+        x.data_ptr(), tokens, k, ldx, x_scale2.data_ptr(), w_hat.data_ptr(), o, ldw, out.data_ptr(), ldy,
+        workspace.data_ptr(), workspace.numel(), _stream(x)))
     return out

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4mi.so")
-SOURCES = ["api.hip", "quant.hip", "hessian.hip", "sweep.hip", "cast.hip", "fp8.hip", "rotate.hip"]
+SOURCES = ["api.hip", "quant.hip", "hessian.hip", "sweep.hip", "cast.hip", "fp8.hip", "rotate.hip", "linear.hip"]
 ARCH = os.environ.get("NVFP4MI_ARCH", "gfx950")
 
 FLAGS = [
@@ -27,6 +27,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]
+# hipBLASLt serves the plain bf16 GEMM of the QuantLinear forward
+LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def _hipcc() -> str:
@@ -56,7 +58,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, *LINK]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

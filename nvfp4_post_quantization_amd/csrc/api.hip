@@ -1,6 +1,7 @@
 // C ABI entry points (include/nvfp4mi.h): argument validation on the host,
 // then the launches.  No HIP call happens before validation succeeds, so
 // every error code except NVFP4_ERR_HIP can be produced without a GPU.
+#include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -13,6 +14,13 @@ static thread_local char g_hip_error[256] = "no HIP error recorded";
 
 void set_hip_error(hipError_t e, const char* where) {
   snprintf(g_hip_error, sizeof g_hip_error, "HIP error in %s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+void set_error_text(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_hip_error, sizeof g_hip_error, fmt, ap);
+  va_end(ap);
 }
 
 int force_exact_flag() {
@@ -195,6 +203,43 @@ int nvfp4_hessian_hadamard(const float* H, int64_t groups, float* H_out, void* s
   if (groups == 0) return NVFP4_OK;
   if (!H || !H_out) return NVFP4_ERR_NULL_ARG;
   return launch_hessian_hadamard(H, groups, H_out, as_stream(stream));
+}
+
+int nvfp4_fakequant(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2, uint16_t* out,
+                    int64_t ldo, void* stream) {
+  int st = check_matrix(rows, k, ldx, 2);
+  if (st) return st;
+  if ((st = check_matrix(rows, k, ldo, 2))) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!scale2 || ((!x || !out) && rows > 0)) return NVFP4_ERR_NULL_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx)) || (st = check_bf16_rows(out, ldo))) return st;
+  return launch_fakequant(x, rows, k, ldx, scale2, out, ldo, as_stream(stream));
+}
+
+size_t nvfp4_quantlinear_workspace_bytes(int64_t tokens, int64_t k) {
+  if (tokens < 0 || k <= 0 || (k % 16) != 0 || !mul_fits(tokens, k) || !mul_fits(tokens * k, 2)) return 0;
+  return quantlinear_workspace_bytes(tokens, k);
+}
+
+int nvfp4_quantlinear_forward(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* x_scale2,
+                              const uint16_t* w, int64_t out_features, int64_t ldw, uint16_t* y, int64_t ldy,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_matrix(tokens, k, ldx, 2);
+  if (st) return st;
+  if ((st = check_matrix(out_features, k, ldw, 2))) return st;
+  if (out_features <= 0) return NVFP4_ERR_BAD_SHAPE;
+  if ((st = check_matrix(tokens, out_features, ldy, 2))) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!x_scale2 || !w || ((!x || !y) && tokens > 0)) return NVFP4_ERR_NULL_ARG;
+  if (tokens == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx)) || (st = check_bf16_rows(w, ldw)) || (st = check_bf16_rows(y, ldy))) return st;
+  const size_t need = quantlinear_workspace_bytes(tokens, k);
+  if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!workspace) return NVFP4_ERR_NULL_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return NVFP4_ERR_MISALIGNED;
+  return launch_quantlinear(x, tokens, k, ldx, x_scale2, w, out_features, ldw, y, ldy, workspace,
+                            as_stream(stream));
 }
 
 }  // extern "C"

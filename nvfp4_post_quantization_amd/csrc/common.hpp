@@ -48,6 +48,14 @@ int launch_fp8_dequant(const uint8_t* q, const float* scale, int64_t rows, int64
 int launch_block_hadamard(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint16_t* out, int64_t ldo,
                           hipStream_t s);
 int launch_hessian_hadamard(const float* H, int64_t groups, float* Hout, hipStream_t s);
+int launch_fakequant(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2, uint16_t* out,
+                     int64_t ldo, hipStream_t s);
+size_t quantlinear_workspace_bytes(int64_t tokens, int64_t k);
+int launch_quantlinear(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* x_scale2,
+                       const uint16_t* w, int64_t out_features, int64_t ldw, uint16_t* y, int64_t ldy,
+                       void* workspace, hipStream_t s);
+// printf-style text for the next nvfp4_status_string(NVFP4_ERR_HIP) on this thread
+void set_error_text(const char* fmt, ...);
 int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
                        const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s);
 int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,

@@ -13,6 +13,9 @@
 // the elements are then quantized with the certified fast path or the exact
 // threshold path (nvfp4_device.hpp).
 //
+// Fake QDQ ("NVFP4 量化流程说明" §2.2, the QuantLinear input quantizer): the
+// dynamic quantizer followed by the two-DQ chain in the same lane, bf16 out.
+//
 // Dequant ("NVFP4 量化流程说明" §5.4): DQ1 d = RN_f32(e4m3 * scale_2),
 // DQ2 RN_f32(e2m1 * d), cast to BF16 (v_cvt_pk_bf16_f32, nearest even); one
 // lane per half block.
@@ -154,11 +157,31 @@ struct BlockPos {
   }
 };
 
+// bf16 of RN_f32(e2m1 * d) for the 8 nibbles of one word (the two-DQ chain).
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, float d) {
+  float a0, b0, a1, b1, a2, b2, a3, b3;
+  fp4x2_to_f32<0>(w, a0, b0);
+  fp4x2_to_f32<1>(w, a1, b1);
+  fp4x2_to_f32<2>(w, a2, b2);
+  fp4x2_to_f32<3>(w, a3, b3);
+  const f32x2 v0 = {a0 * d, b0 * d}, v1 = {a1 * d, b1 * d}, v2 = {a2 * d, b2 * d}, v3 = {a3 * d, b3 * d};
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2)));
+}
+
+// FQ = false: packed nibbles + block codes (the dynamic quantizer).  FQ = true:
+// the fake QDQ, i.e. the same quantization followed by the two-DQ chain,
+// written as bf16 [rows][ldo] without the packed intermediate.
+template <bool FQ>
 __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                int64_t k, int64_t ldx,
                                                                const float* __restrict__ scale2,
                                                                uint8_t* __restrict__ packed,
-                                                               uint8_t* __restrict__ codes, int force_exact) {
+                                                               uint8_t* __restrict__ codes,
+                                                               uint16_t* __restrict__ out, int64_t ldo,
+                                                               int force_exact) {
   __shared__ CodeTables t;
   __shared__ int32_t tp[128];
   const int64_t nb = k >> 4;
@@ -209,8 +232,15 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
         const uint32_t P = max((uint32_t)m2.x, (uint32_t)m2.y);
         const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
         const uint2 q = quantize_block(wv[j], c, t, mode);
-        *reinterpret_cast<uint2*>(packed + pos.r * (k >> 1) + pos.g * 8) = q;
-        codes[pos.r * nb + pos.g] = (uint8_t)c;
+        if constexpr (FQ) {
+          const float d = t.d[c];
+          uint4* dst = reinterpret_cast<uint4*>(out + pos.r * ldo + pos.g * 16);
+          dst[0] = dequant_word(q.x, d);
+          dst[1] = dequant_word(q.y, d);
+        } else {
+          *reinterpret_cast<uint2*>(packed + pos.r * (k >> 1) + pos.g * 8) = q;
+          codes[pos.r * nb + pos.g] = (uint8_t)c;
+        }
       }
       pos.advance(dr, dg, nb);
     }
@@ -225,9 +255,17 @@ static unsigned flat_grid(int64_t rows, int64_t nb) {
 int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
                             uint8_t* packed, uint8_t* codes, hipStream_t s) {
   if (rows == 0) return NVFP4_OK;
-  quantize_dynamic_kernel<<<flat_grid(rows, k >> 4), 256, 0, s>>>(x, rows, k, ldx, scale2, packed, codes,
-                                                                  force_exact_flag());
+  quantize_dynamic_kernel<false><<<flat_grid(rows, k >> 4), 256, 0, s>>>(x, rows, k, ldx, scale2, packed, codes,
+                                                                         nullptr, 0, force_exact_flag());
   return launch_status("quantize_dynamic_kernel");
+}
+
+int launch_fakequant(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2, uint16_t* out,
+                     int64_t ldo, hipStream_t s) {
+  if (rows == 0) return NVFP4_OK;
+  quantize_dynamic_kernel<true><<<flat_grid(rows, k >> 4), 256, 0, s>>>(x, rows, k, ldx, scale2, nullptr, nullptr,
+                                                                        out, ldo, force_exact_flag());
+  return launch_status("fakequant_kernel");
 }
 
 // ---------------------------------------------------------------- dequant ----
@@ -276,19 +314,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
       if (pos.r < rows) {
-        const float d = dt[cc[j]];
-        const uint32_t w = pc[j];
-        float a0, b0, a1, b1, a2, b2, a3, b3;
-        fp4x2_to_f32<0>(w, a0, b0);
-        fp4x2_to_f32<1>(w, a1, b1);
-        fp4x2_to_f32<2>(w, a2, b2);
-        fp4x2_to_f32<3>(w, a3, b3);
-        f32x2 v0 = {a0 * d, b0 * d}, v1 = {a1 * d, b1 * d}, v2 = {a2 * d, b2 * d}, v3 = {a3 * d, b3 * d};
-        *reinterpret_cast<uint4*>(out + pos.r * k + pos.g * 8) =
-            make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2)),
-                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2)),
-                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2)),
-                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2)));
+        *reinterpret_cast<uint4*>(out + pos.r * k + pos.g * 8) = dequant_word(pc[j], dt[cc[j]]);
       }
       pos.advance(dr, dg, nh);
     }

@@ -38,7 +38,8 @@ def test_header_symbols_exported(lib):
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
         "nvfp4_hessian_accum", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
-        "nvfp4_block_hadamard", "nvfp4_hessian_hadamard",
+        "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant",
+        "nvfp4_quantlinear_workspace_bytes", "nvfp4_quantlinear_forward",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -181,3 +182,28 @@ def test_hadamard_validation(lib):
     assert h(None, 4, P, None) == NULL
     assert h(P, 4, None, None) == NULL
     assert h(None, 0, None, None) == OK
+
+
+def test_fakequant_and_forward_validation(lib):
+    f = lib.nvfp4_fakequant
+    assert f(P, 4, 24, 24, P, P, 24, None) == SHAPE             # k % 16
+    assert f(P, 4, 32, 32, None, P, 32, None) == NULL           # scale2
+    assert f(P, 4, 32, 32, P, P, 16, None) == SHAPE             # ldo < k
+    assert f(P + 2, 4, 32, 32, P, P, 32, None) == ALIGN
+    assert f(P, 4, 32, 32, P, P + 2, 32, None) == ALIGN
+    assert f(P, 0, 32, 32, P, None, 32, None) == OK
+    assert lib.nvfp4_quantlinear_workspace_bytes(0, 32) > 0
+    assert lib.nvfp4_quantlinear_workspace_bytes(8, 24) == 0
+    need = lib.nvfp4_quantlinear_workspace_bytes(8, 32)
+    assert need >= 8 * 32 * 2
+    q = lib.nvfp4_quantlinear_forward
+    assert q(P, 8, 24, 24, P, P, 16, 24, P, 16, P, need, None) == SHAPE       # k % 16
+    assert q(P, 8, 32, 32, P, P, 0, 32, P, 16, P, need, None) == SHAPE        # out_features = 0
+    assert q(P, 8, 32, 32, P, P, 16, 32, P, 8, P, need, None) == SHAPE        # ldy < out
+    assert q(P, 8, 32, 32, None, P, 16, 32, P, 16, P, need, None) == NULL     # x_scale2
+    assert q(P, 8, 32, 32, P, None, 16, 32, P, 16, P, need, None) == NULL     # w
+    assert q(P, 8, 32, 32, P, P, 16, 32, P, 16, P, need - 1, None) == WS
+    assert q(P, 8, 32, 32, P, P, 16, 32, P, 16, None, need, None) == NULL     # workspace
+    assert q(P, 8, 32, 32, P, P, 16, 32, P, 16, P + 16, need, None) == ALIGN  # workspace not 256-aligned
+    assert q(P, 8, 32, 32, P, P + 2, 16, 32, P, 16, P, need, None) == ALIGN
+    assert q(P, 0, 32, 32, P, P, 16, 32, None, 16, None, 0, None) == OK       # nothing to do
