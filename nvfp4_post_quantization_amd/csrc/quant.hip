@@ -144,7 +144,9 @@ __device__ __forceinline__ uint2 quantize_block(const uint32_t* wv, int c, const
 }
 
 constexpr int kUnits = 4;                // blocks per thread per batch (loads in flight)
-constexpr int kFlatGrid = 512;           // two workgroups per CU: each builds the code tables once
+constexpr int kQuantGrid = 1024;         // quantizers: four workgroups per CU hide the E2M1 work (measured
+                                         // 23.6 -> 21.0 us on [8192, 4096] against 512)
+constexpr int kDequantGrid = 512;        // dequant: two per CU (1024 measured 9% slower)
 
 // Position of flat block index u (row-major [rows][nb]) advanced by a fixed
 // stride without a 64-bit division per step.
@@ -247,15 +249,15 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
   }
 }
 
-static unsigned flat_grid(int64_t rows, int64_t nb) {
+static unsigned flat_grid(int64_t rows, int64_t nb, int64_t cap) {
   const int64_t want = (rows * nb + 256 * kUnits - 1) / (256 * kUnits);
-  return (unsigned)(want < kFlatGrid ? (want > 0 ? want : 1) : kFlatGrid);
+  return (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
 }
 
 int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
                             uint8_t* packed, uint8_t* codes, hipStream_t s) {
   if (rows == 0) return NVFP4_OK;
-  quantize_dynamic_kernel<false><<<flat_grid(rows, k >> 4), 256, 0, s>>>(x, rows, k, ldx, scale2, packed, codes,
+  quantize_dynamic_kernel<false><<<flat_grid(rows, k >> 4, kQuantGrid), 256, 0, s>>>(x, rows, k, ldx, scale2, packed, codes,
                                                                          nullptr, 0, force_exact_flag());
   return launch_status("quantize_dynamic_kernel");
 }
@@ -263,7 +265,7 @@ int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t 
 int launch_fakequant(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2, uint16_t* out,
                      int64_t ldo, hipStream_t s) {
   if (rows == 0) return NVFP4_OK;
-  quantize_dynamic_kernel<true><<<flat_grid(rows, k >> 4), 256, 0, s>>>(x, rows, k, ldx, scale2, nullptr, nullptr,
+  quantize_dynamic_kernel<true><<<flat_grid(rows, k >> 4, kQuantGrid), 256, 0, s>>>(x, rows, k, ldx, scale2, nullptr, nullptr,
                                                                         out, ldo, force_exact_flag());
   return launch_status("fakequant_kernel");
 }
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 int launch_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2, int64_t rows, int64_t k,
                    uint16_t* out, hipStream_t s) {
   if (rows == 0) return NVFP4_OK;
-  dequant_kernel<<<flat_grid(rows, k >> 3), 256, 0, s>>>(packed, codes, scale2, rows, k, out);
+  dequant_kernel<<<flat_grid(rows, k >> 3, kDequantGrid), 256, 0, s>>>(packed, codes, scale2, rows, k, out);
   return launch_status("dequant_kernel");
 }
 
