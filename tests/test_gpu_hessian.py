@@ -89,3 +89,14 @@ def test_hessian_outlier_channels_precision():
     x = rng.laplace(0, 1, (65536, 256))
     x[:, [3, 77, 200]] *= 40.0
     _check(datagen.f32_to_bf16_bits(x.astype(np.float32)))
+
+
+@pytest.mark.parametrize("t,k", [(130, 66048), (700, 65664), (65, 98304)])
+def test_hessian_wide_k_ranges_cross_slabs(t, k):
+    """At least as many slabs as workgroups: work ranges cross slab
+    boundaries, so workgroups write up to three partial slots and the reduce
+    combines several owners per group."""
+    note(f"hessian wide k t={t} k={k}")
+    rng = np.random.default_rng(t + k)
+    x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (t, k)).astype(np.float32))
+    _check(x)

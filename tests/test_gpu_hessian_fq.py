@@ -192,3 +192,13 @@ def test_fq_full_chunks(stream_id):
     err = rel_frobenius(host(H)[gs], ref)
     assert err.max() <= TOL, f"max rel Frobenius error {err.max():.3e}"
     assert float(host(amax)[0]) == amax_ref
+
+
+@pytest.mark.parametrize("t,k", [(130, 132096), (200, 131200)])
+def test_fq_wide_k_ranges_cross_slabs(t, k):
+    """The fake-quant kernel's larger grid: more slabs than its workgroups,
+    so work ranges cross slab boundaries (multi-slot partials)."""
+    note(f"hessian_fq wide k t={t} k={k}")
+    rng = np.random.default_rng(t * k)
+    x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (t, k)).astype(np.float32))
+    _check(x)
