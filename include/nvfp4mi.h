@@ -13,8 +13,11 @@
  * ------------------
  * - Every pointer argument is a DEVICE pointer (hipMalloc'ed or from a
  *   framework allocator) owned by the caller, unless stated otherwise.  The
- *   library keeps no pointer after a call returns and never allocates device
- *   memory; scratch memory comes in as a caller-provided workspace.
+ *   library keeps no pointer after a call returns and allocates no device
+ *   memory of its own, except the hipBLASLt handle that
+ *   nvfp4_quantlinear_forward creates on its first call on a device (kept
+ *   until the process ends); scratch memory comes in as a caller-provided
+ *   workspace.
  * - bf16 values are passed as uint16_t bit patterns.  Matrices are row-major;
  *   "ld" arguments are row strides in ELEMENTS.  Blocks of 16 run along the
  *   last (contiguous) axis.
@@ -54,7 +57,8 @@ enum nvfp4_status {
   NVFP4_ERR_NULL_ARG = 1,     /* a required pointer is NULL                         */
   NVFP4_ERR_BAD_SHAPE = 2,    /* a size is negative, k % 16 != 0 (k % 32 for the
                                  cast), ld < k, or a product overflows int64       */
-  NVFP4_ERR_MISALIGNED = 3,   /* a bf16/byte matrix row is not 16-byte aligned       */
+  NVFP4_ERR_MISALIGNED = 3,   /* a buffer or matrix row is not aligned as the
+                                 function requires (16 bytes for bf16 rows)       */
   NVFP4_ERR_WORKSPACE = 4,    /* workspace smaller than the matching *_bytes() query */
   NVFP4_ERR_BAD_INPUT = 5,    /* an argument value is out of range (e.g. mats <= 0)  */
   NVFP4_ERR_HIP = 6           /* a HIP launch or API call failed                     */
@@ -81,9 +85,9 @@ int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out,
                          float* amax_out, void* stream);
 
 /*
- * Bytes of workspace nvfp4_hessian_accum needs for (tokens, k); 0 when
- * tokens == 0.  Returns 0 for invalid sizes too (the accumulate call then
- * reports the shape error).
+ * Bytes of workspace nvfp4_hessian_accum and nvfp4_hessian_accum_fq need for
+ * (tokens, k) (one size serves both); 0 when tokens == 0.  Returns 0 for
+ * invalid sizes too (the accumulate call then reports the shape error).
  */
 size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k);
 

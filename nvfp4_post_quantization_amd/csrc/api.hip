@@ -55,7 +55,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL_ARG: return "a required pointer argument is NULL";
     case NVFP4_ERR_BAD_SHAPE: return "bad shape: negative size, k not a multiple of the block, ld < k, or size overflow";
-    case NVFP4_ERR_MISALIGNED: return "misaligned buffer: rows must start on 16-byte boundaries";
+    case NVFP4_ERR_MISALIGNED: return "misaligned buffer: a pointer or row stride breaks the function's alignment rule";
     case NVFP4_ERR_WORKSPACE: return "workspace smaller than the size the matching *_bytes query returns";
     case NVFP4_ERR_BAD_INPUT: return "argument value out of range";
     case NVFP4_ERR_HIP: return g_hip_error;
