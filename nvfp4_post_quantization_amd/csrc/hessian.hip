@@ -44,6 +44,7 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __host__ __device__ inline int64_t cdiv(int64_t n, int64_t d) { return (n + d - 1) / d; }
 
@@ -234,10 +235,29 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           u16x8 v;
+          if constexpr (QM >= 0) {
+            // fake-quant kernel (ALU-heavier: measured 5-10% faster this way):
+            // two transposing reads; lane jj of each 16-lane group fetches 4
+            // channels (4*(jj&3)..+3 of the group) of token R0 + jj/4, and
+            // after the transpose lane ch holds its channel at 4 consecutive
+            // tokens, the same 8 values in the same order as the plain reads
+            const int jj = lane & 15;
+            const int c4 = gl * 16 + 4 * (jj & 3);
+            const int R0 = 32 * m + 8 * q + (jj >> 2);
+            const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)&tile[R0 * kSlabCols + swz(c4 >> 3, R0) * 8 + (c4 & 7)]);
+            const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)&tile[(R0 + 4) * kSlabCols + swz(c4 >> 3, R0 + 4) * 8 +
+                                                                (c4 & 7)]);
+            v = __builtin_bit_cast(u16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            // plain kernel: 2-byte reads (the transposing reads measured 2%
+            // slower at K = 12288 here)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int R = 32 * m + 8 * q + e;
-            v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
+            for (int e = 0; e < 8; ++e) {
+              const int R = 32 * m + 8 * q + e;
+              v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
+            }
           }
           if (QM < 0 && want_amax) {
             const u32x4 d = __builtin_bit_cast(u32x4, v);
