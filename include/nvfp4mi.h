@@ -168,6 +168,21 @@ int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw,
                       uint8_t* codes, float* cost, void* stream);
 
 /*
+ * nvfp4_scale_sweep with an occupancy cap, for running the sweep beside an
+ * HBM-bound kernel on another stream (e.g. nvfp4_hessian_accum of the next
+ * calibration stream).  wgs_per_cu = 0: as nvfp4_scale_sweep (as many
+ * workgroups per CU as fit); 1: at most one sweep workgroup per CU, by
+ * reserving just over half of the CU's LDS per workgroup, which leaves the
+ * rest of the LDS and 272 VGPRs per SIMD to the other kernel.  Results are
+ * identical to nvfp4_scale_sweep's.  The reservation is sized once per
+ * process for the current device.
+ * Errors: as nvfp4_scale_sweep, plus BAD_INPUT (wgs_per_cu not 0 or 1).
+ */
+int nvfp4_scale_sweep_ex(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw,
+                         const float* H, const float* scale2, uint8_t* packed,
+                         uint8_t* codes, float* cost, int wgs_per_cu, void* stream);
+
+/*
  * Dynamic per-16 NVFP4 activation quantizer ("NVFP4 量化流程说明" §3.4-§3.5):
  * per block, amax_b = max |x| over the 16 elements, code =
  * RNE_sat(amax_b / (6 * scale_2)) on the E4M3 grid (raised to 0x01 if the

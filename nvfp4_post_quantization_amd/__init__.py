@@ -41,6 +41,8 @@ _SIGS = {
                                               _c_void_p, ctypes.c_size_t, _c_void_p]),
     "nvfp4_scale_sweep": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                          _c_void_p, _c_void_p, _c_void_p]),
+    "nvfp4_scale_sweep_ex": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                            _c_void_p, _c_void_p, ctypes.c_int, _c_void_p]),
     "nvfp4_quantize_dynamic": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                               _c_void_p]),
     "nvfp4_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
@@ -186,8 +188,11 @@ def hessian_accum_fq(x: torch.Tensor, scale2: torch.Tensor, H: torch.Tensor, ama
 
 
 def scale_sweep(w: torch.Tensor, H: torch.Tensor, scale2: torch.Tensor, want_cost: bool = False,
-                out=None):
-    """Hessian-weighted sweep of the E4M3 block scale of bf16 w[rows, k]."""
+                out=None, wgs_per_cu: int = 0, stream: torch.cuda.Stream | None = None):
+    """Hessian-weighted sweep of the E4M3 block scale of bf16 w[rows, k].
+
+    wgs_per_cu = 1 caps the sweep at one workgroup per CU (to run beside an
+    HBM-bound kernel on another stream); stream defaults to the current one."""
     _dev(w, torch.bfloat16, "w", 2)
     _dev(H, torch.float32, "H")
     _dev(scale2, torch.float32, "scale2")
@@ -201,9 +206,10 @@ def scale_sweep(w: torch.Tensor, H: torch.Tensor, scale2: torch.Tensor, want_cos
         cost = torch.empty((rows, k // 16), dtype=torch.float32, device=w.device) if want_cost else None
     else:
         packed, codes, cost = out
-    _check("nvfp4_scale_sweep", load().nvfp4_scale_sweep(
+    sp = stream.cuda_stream if stream is not None else _stream(w)
+    _check("nvfp4_scale_sweep_ex", load().nvfp4_scale_sweep_ex(
         w.data_ptr(), rows, k, ldw, H.data_ptr(), scale2.data_ptr(), packed.data_ptr(), codes.data_ptr(),
-        cost.data_ptr() if cost is not None else None, _stream(w)))
+        cost.data_ptr() if cost is not None else None, int(wgs_per_cu), sp))
     return packed, codes, cost
 
 

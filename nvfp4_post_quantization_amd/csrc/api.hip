@@ -107,15 +107,26 @@ int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t
   return launch_hessian_accum_fq(x, tokens, k, ldx, scale2, H, amax_inout, workspace, as_stream(stream));
 }
 
-int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
-                      uint8_t* packed, uint8_t* codes, float* cost, void* stream) {
+static int scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
+                       uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu, void* stream) {
   int st = check_matrix(rows, k, ldw, 2);
   if (st) return st;
   if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (wgs_per_cu < 0 || wgs_per_cu > 1) return NVFP4_ERR_BAD_INPUT;
   if (!H || !scale2 || ((!w || !packed || !codes) && rows > 0)) return NVFP4_ERR_NULL_ARG;
   if (rows == 0) return NVFP4_OK;
   if ((st = check_bf16_rows(w, ldw))) return st;
-  return launch_scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, as_stream(stream));
+  return launch_scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, wgs_per_cu, as_stream(stream));
+}
+
+int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
+                      uint8_t* packed, uint8_t* codes, float* cost, void* stream) {
+  return scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, 0, stream);
+}
+
+int nvfp4_scale_sweep_ex(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
+                         uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu, void* stream) {
+  return scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, wgs_per_cu, stream);
 }
 
 int nvfp4_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,

@@ -57,7 +57,8 @@ int launch_quantlinear(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx
 // printf-style text for the next nvfp4_status_string(NVFP4_ERR_HIP) on this thread
 void set_error_text(const char* fmt, ...);
 int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
-                       const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s);
+                       const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu,
+                       hipStream_t s);
 int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,
                    uint8_t* codes, float* scale2, int64_t* fallback, hipStream_t s);
 

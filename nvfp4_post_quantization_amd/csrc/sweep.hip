@@ -260,8 +260,32 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
 
 }  // namespace
 
+// LDS to reserve per workgroup so that at most one sweep workgroup fits on a
+// CU: half the CU's LDS plus 1 KiB, less what the kernel declares.  The rest
+// of the CU (just under half its LDS, and 272 of 512 VGPRs per SIMD beside
+// the sweep's one wave) stays free for a kernel on another stream.
+static int query_one_per_cu_lds() {
+  int dev = 0, lds_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+  hipFuncAttributes fa;
+  if (e == hipSuccess) e = hipFuncGetAttributes(&fa, (const void*)sweep_kernel);
+  const int want = lds_cu / 2 + 1024 - (int)fa.sharedSizeBytes;
+  if (e == hipSuccess) e = hipFuncSetAttribute((const void*)sweep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  if (e != hipSuccess) { set_hip_error(e, "sweep LDS reservation"); return -1; }
+  return want;
+}
+
+static int one_per_cu_lds(unsigned* dyn) {
+  static const int want = query_one_per_cu_lds();          // once per process (thread-safe initialisation)
+  if (want < 0) return NVFP4_ERR_HIP;
+  *dyn = (unsigned)want;
+  return NVFP4_OK;
+}
+
 int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
-                       const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, hipStream_t s) {
+                       const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu,
+                       hipStream_t s) {
   const int64_t groups = k >> 4;
   const int64_t gx = (groups + kWaves - 1) / kWaves;
   // rows per workgroup: a multiple of 64 (one row per lane), about 4096 workgroups
@@ -273,8 +297,13 @@ int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, 
     rpw *= 2;
     chunks = (rows + rpw - 1) / rpw;
   }
+  unsigned dyn = 0;
+  if (wgs_per_cu == 1) {
+    const int st = one_per_cu_lds(&dyn);
+    if (st) return st;
+  }
   dim3 grid((unsigned)gx, (unsigned)chunks, 1);
-  sweep_kernel<<<grid, kThreads, 0, s>>>(w, rows, k, ldw, H, scale2, rpw, packed, codes, cost, force_exact_flag());
+  sweep_kernel<<<grid, kThreads, dyn, s>>>(w, rows, k, ldw, H, scale2, rpw, packed, codes, cost, force_exact_flag());
   return launch_status("sweep_kernel");
 }
 

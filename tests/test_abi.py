@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
         "nvfp4_hessian_accum", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
-        "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant",
+        "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant", "nvfp4_scale_sweep_ex",
         "nvfp4_quantlinear_workspace_bytes", "nvfp4_quantlinear_forward",
     }
     for n in names:
@@ -207,3 +207,12 @@ def test_fakequant_and_forward_validation(lib):
     assert q(P, 8, 32, 32, P, P, 16, 32, P, 16, P + 16, need, None) == ALIGN  # workspace not 256-aligned
     assert q(P, 8, 32, 32, P, P + 2, 16, 32, P, 16, P, need, None) == ALIGN
     assert q(P, 0, 32, 32, P, P, 16, 32, None, 16, None, 0, None) == OK       # nothing to do
+
+
+def test_sweep_ex_validation(lib):
+    s = lib.nvfp4_scale_sweep_ex
+    assert s(P, 4, 32, 32, P, P, P, P, None, 2, None) == BADIN     # wgs_per_cu
+    assert s(P, 4, 32, 32, P, P, P, P, None, -1, None) == BADIN
+    assert s(P, 4, 24, 24, P, P, P, P, None, 1, None) == SHAPE
+    assert s(P, 4, 32, 32, None, P, P, P, None, 1, None) == NULL
+    assert s(P, 0, 32, 32, P, P, None, None, None, 1, None) == OK
