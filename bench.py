@@ -12,7 +12,9 @@ inputs:
          (9,437,184 blocks);
   * activations X [8192, 4096]: a1 amax, a4 dynamic NVFP4 quantization and
     a5 the dequant round trip;
-  * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast.
+  * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast
+    (in place on the nibbles, so each step first restores the original
+    nibbles of the fallback blocks, ~9 MB, inside the timed step).
 After the timed steps, two neighbouring pieces are timed on their own and
 reported under stages (not part of the step): the W4A4 form of a2 (Hessian
 of the fake-quantized calibration streams, next_w4a4_hessian), the FP8 E4M3
@@ -108,7 +110,15 @@ def main():
     P5 = torch.from_numpy(p5_host).to(dev)
     E5 = torch.from_numpy(e5_host).to(dev)
     n_forced = int(forced5.sum())
-    del p5_host, e5_host, forced5
+    # The cast rewrites the nibbles of its fallback blocks in place; each step
+    # first puts back their original 16 bytes so that every step casts the
+    # same input (fallback: k_max - k_j > 17 within an expert's pair).
+    k5 = e5_host.astype(np.int16) - 127
+    kmax5 = k5.reshape(k5.shape[0], -1).max(axis=1)
+    fb_idx = torch.from_numpy(np.flatnonzero((kmax5[:, None, None, None] - k5).reshape(-1) > 17)).to(dev)
+    P5_blocks = P5.view(-1, 16)
+    P5_fb_orig = P5_blocks.index_select(0, fb_idx)
+    del p5_host, e5_host, forced5, k5
     log(f"all inputs resident ({time.time() - t0:.1f}s)")
 
     # ------------------------------------------------------------ outputs / state
@@ -136,6 +146,7 @@ def main():
 
     side = torch.cuda.Stream(device=dev)                         # default priority
     sptr_b = side.cuda_stream
+    streams = {sptr: stream, sptr_b: side}
 
     def stage_calls(name, sp):
         """The calls of one stage (all but a2), enqueued on stream pointer sp."""
@@ -151,6 +162,8 @@ def main():
             chk("dequant", lib.nvfp4_dequant(q3[0].data_ptr(), q3[1].data_ptr(), s2x3.data_ptr(), 8192, 4096,
                                              dq3.data_ptr(), sp))
         elif name == "a6_cast":
+            with torch.cuda.stream(streams[sp]):
+                P5_blocks.index_copy_(0, fb_idx, P5_fb_orig)
             chk("cast", lib.mxfp4_to_nvfp4_cast(P5.data_ptr(), E5.data_ptr(), 128, 2, 2048, 7168, c5[0].data_ptr(),
                                                 c5[1].data_ptr(), c5[2].data_ptr(), sp))
 
@@ -237,8 +250,14 @@ def main():
     h_call_ms = sum(a.elapsed_time(b) for ev in evs for hs in ev["h"] for a, b in hs) / (args.steps * 32)
 
     # the overlapped schedule must produce exactly what the serial order does
-    snap = [t.clone() for t in (H[0], H[1], amax_x[0], amax_x[1], q3[0], q3[1], dq3, c5[0], c5[1], c5[2],
-                                *[o for n in W for o in sw_out[n]])]
+    def outputs():
+        d = {"H0": H[0], "H1": H[1], "amax_x0": amax_x[0], "amax_x1": amax_x[1], "q3_packed": q3[0],
+             "q3_codes": q3[1], "dq3": dq3, "c5_packed": c5[0], "c5_scale2": c5[1], "c5_fallbacks": c5[2]}
+        for n in W:
+            d[f"{n}_packed"], d[f"{n}_codes"] = sw_out[n]
+        return d
+
+    snap = {k: t.clone() for k, t in outputs().items()}
     # per-stage times from the same work in stage order on one stream
     n_serial = max(1, min(args.steps, 5))
     evs_serial = [new_events(serial=True) for _ in range(n_serial)]
@@ -246,9 +265,9 @@ def main():
     for i in range(n_serial):
         step_serial(evs_serial[i])
     torch.cuda.synchronize()
-    again = [H[0], H[1], amax_x[0], amax_x[1], q3[0], q3[1], dq3, c5[0], c5[1], c5[2], *[o for n in W for o in sw_out[n]]]
-    if not all(torch.equal(a, b) for a, b in zip(snap, again)):
-        raise RuntimeError("overlapped step differs from the serial step")
+    differ = {k: int((t != snap[k]).sum().item()) for k, t in outputs().items() if not torch.equal(t, snap[k])}
+    if differ:
+        raise RuntimeError(f"overlapped step differs from the serial step (differing elements: {differ})")
 
     # per-stage times (ms per step, averaged over the serial steps)
     st_ms = {k: 0.0 for k in stages}
@@ -266,7 +285,7 @@ def main():
     x_bytes = sum(x.numel() * 2 for xs in X for x in xs)
     a1_bytes = sum(w.numel() * 2 for w in W.values()) + x3.numel() * 2
     q_bytes = x3.numel() * 2.5625
-    cast_bytes = E5.numel() + c5[0].numel() + fb * C5_FALLBACK_BYTES
+    cast_bytes = E5.numel() + c5[0].numel() + fb * C5_FALLBACK_BYTES     # the restore of the inputs not counted
     flops = blocks * SWEEP_FLOP_PER_BLOCK
     info = {
         "a1_scale2": dict(launches=4, bytes=a1_bytes),
