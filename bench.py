@@ -25,9 +25,10 @@ of one calibration chunk through the swept gate weight
 (next_quantlinear_forward).
 
 The headline value is weight blocks swept per second of whole-step time.
-In the timed steps the gate/up sweeps and a4-a6 run on a second HIP stream
-while the Hessian of the second calibration stream runs (they need only the
-first stream's H); those two sweeps are capped at one workgroup per CU so
+In the timed steps a1 runs on a second HIP stream beside the first
+calibration stream's Hessian, and then the gate/up sweeps and a4-a6 run on
+it while the Hessian of the second calibration stream runs (they need only
+the first stream's H); those two sweeps are capped at one workgroup per CU so
 that the Hessian keeps its own workgroups resident beside them.  One serial
 step afterwards must reproduce every output bit for bit.  Per-stage times
 come from HIP events over the same work in stage order on one stream.
@@ -203,12 +204,15 @@ def main():
             ev[k].record(stream)
 
     def step(ev):
-        """The timed step: the same work, with the ALU-bound gate/up sweeps and
-        the small a4-a6 passes on a second stream while the HBM-bound Hessian
-        of the down-projection stream runs (they only need the first
-        stream's H and the scales)."""
+        """The timed step: the same work on two streams.  The second stream
+        takes a1 while the first calibration stream's Hessian starts, then
+        (once that H is done) the ALU-bound gate/up sweeps and the small
+        a4-a6 passes while the HBM-bound Hessian of the down-projection
+        stream runs; the down sweep follows on the first stream."""
         ev["start"].record(stream)
-        stage_calls("a1_scale2", sptr)
+        side.wait_event(ev["start"])                             # the previous step is done
+        stage_calls("a1_scale2", sptr_b)
+        ev["a1_done"].record(side)
         for s in (0, 1):
             H[s].zero_()
             amax_x[s].zero_()
@@ -221,6 +225,7 @@ def main():
         for k in ("a4_quantize", "a5_dequant", "a6_restore", "a6_cast"):
             stage_calls(k, sptr_b)
         ev["side_done"].record(side)
+        stream.wait_event(ev["a1_done"])                         # scale_2 of the down weight
         sweep("down", sptr)
         stream.wait_event(ev["side_done"])
         ev["end"].record(stream)
@@ -230,7 +235,7 @@ def main():
         h = [(E(), E()) for s in (0, 1)]
         if serial:
             return dict({k: E() for k in ["start"] + marks}, h=h)
-        return {"start": E(), "h0_done": E(), "side_done": E(), "end": E(), "h": h}
+        return {"start": E(), "a1_done": E(), "h0_done": E(), "side_done": E(), "end": E(), "h": h}
 
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
@@ -543,10 +548,11 @@ def main():
             "calibration_tokens": datagen.C4_TOKENS,
             "chunk_tokens": datagen.C4_CHUNK,
             "parallelism": "single GPU",
-            "schedule": "timed steps: a1, a2 of both calibration streams and the down-weight sweep on one HIP "
-                        "stream; the gate/up sweeps (capped at one workgroup per CU) and a4-a6 on a second "
-                        "stream once the first stream's H is done (checked bit-exact against the serial order); "
-                        "stages: the same work in stage order on one stream",
+            "schedule": "timed steps: a2 of both calibration streams and the down-weight sweep on one HIP "
+                        "stream; a1 on a second stream beside the first calibration stream's Hessian, then the "
+                        "gate/up sweeps (capped at one workgroup per CU) and a4-a6 on it once that H is done "
+                        "(checked bit-exact against the serial order); stages: the same work in stage order "
+                        "on one stream",
             "serial_step_ms": round(step_ms, 4),
         },
         "roofline": roof,
