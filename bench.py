@@ -77,9 +77,9 @@ def log(msg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md for how the work would shard).",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported. The library has no "
+              "multi-GPU path: the Hessian would shard over tokens with one all-reduce of H, and the sweep, "
+              "quantizers and cast over rows or experts with no exchange.", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
