@@ -25,13 +25,16 @@ of one calibration chunk through the swept gate weight
 (next_quantlinear_forward).
 
 The headline value is weight blocks swept per second of whole-step time.
-In the timed steps a1 runs on a second HIP stream beside the first
-calibration stream's Hessian, and then the gate/up sweeps and a4-a6 run on
-it while the Hessian of the second calibration stream runs (they need only
-the first stream's H); those two sweeps are capped at one workgroup per CU so
-that the Hessian keeps its own workgroups resident beside them.  One serial
-step afterwards must reproduce every output bit for bit.  Per-stage times
-come from HIP events over the same work in stage order on one stream.
+In the timed steps one HIP stream accumulates the Hessians and a second runs
+everything else: a1 and a4-a6, the gate/up sweeps once the first
+calibration stream's H is done (beside the second stream's Hessian), and
+the down sweep once the second H is done (beside the next step's first
+Hessian: consecutive steps alternate between two sets of H, amax and
+scale_2 buffers).  Every sweep there is capped at one workgroup per CU so
+that the Hessian keeps its own workgroups resident beside it.  Both buffer
+sets must hold identical results, and one serial step afterwards must
+reproduce every output bit for bit.  Per-stage times come from HIP events
+over the same work in stage order on one stream.
 The roofline entry is the stage with the largest share of the step; for the
 Hessian it gives the live per-call rate in the timed steps and, under
 "alone", the rate of the same calls in the serial pass.  The
@@ -125,12 +128,15 @@ def main():
     # ------------------------------------------------------------ outputs / state
     f32 = dict(dtype=torch.float32, device=dev)
     u8 = dict(dtype=torch.uint8, device=dev)
-    H = {0: torch.zeros((256, 16, 16), **f32), 1: torch.zeros((768, 16, 16), **f32)}
-    amax_x = {0: torch.zeros(1, **f32), 1: torch.zeros(1, **f32)}
+    NB = 2
+    Hb = [{0: torch.zeros((256, 16, 16), **f32), 1: torch.zeros((768, 16, 16), **f32)} for _ in range(NB)]
+    amax_xb = [{0: torch.zeros(1, **f32), 1: torch.zeros(1, **f32)} for _ in range(NB)]
+    H, amax_x = Hb[0], amax_xb[0]
     ws_bytes = max(nq.hessian_workspace_bytes(datagen.C4_CHUNK, k) for k in (4096, 12288))
     ws = torch.empty(ws_bytes, **u8)
-    s2w = {n: torch.zeros(1, **f32) for n in W}
-    amw = {n: torch.zeros(1, **f32) for n in W}
+    s2wb = [{n: torch.zeros(1, **f32) for n in W} for _ in range(NB)]
+    amwb = [{n: torch.zeros(1, **f32) for n in W} for _ in range(NB)]
+    s2w, amw = s2wb[0], amwb[0]
     sw_out = {n: (torch.empty((w.shape[0], w.shape[1] // 2), **u8),
                   torch.empty((w.shape[0], w.shape[1] // 16), **u8)) for n, w in W.items()}
     s2x3, amx3 = torch.zeros(1, **f32), torch.zeros(1, **f32)
@@ -150,12 +156,12 @@ def main():
     sptr_b = side.cuda_stream
     streams = {sptr: stream, sptr_b: side}
 
-    def stage_calls(name, sp):
+    def stage_calls(name, sp, b=0):
         """The calls of one stage (all but a2), enqueued on stream pointer sp."""
         if name == "a1_scale2":
             for n, w in W.items():
-                chk("scale2", lib.nvfp4_compute_scale2(w.data_ptr(), w.numel(), s2w[n].data_ptr(), amw[n].data_ptr(),
-                                                       sp))
+                chk("scale2", lib.nvfp4_compute_scale2(w.data_ptr(), w.numel(), s2wb[b][n].data_ptr(),
+                                                       amwb[b][n].data_ptr(), sp))
             chk("scale2", lib.nvfp4_compute_scale2(x3.data_ptr(), x3.numel(), s2x3.data_ptr(), amx3.data_ptr(), sp))
         elif name == "a4_quantize":
             chk("quantize", lib.nvfp4_quantize_dynamic(x3.data_ptr(), 8192, 4096, 4096, s2x3.data_ptr(),
@@ -170,19 +176,21 @@ def main():
             chk("cast", lib.mxfp4_to_nvfp4_cast(P5.data_ptr(), E5.data_ptr(), 128, 2, 2048, 7168, c5[0].data_ptr(),
                                                 c5[1].data_ptr(), c5[2].data_ptr(), sp))
 
-    def sweep(n, sp, wgs_per_cu=0):
+    def sweep(n, sp, wgs_per_cu=0, b=0):
         w = W[n]
         p, c = sw_out[n]
-        chk("sweep", lib.nvfp4_scale_sweep_ex(w.data_ptr(), w.shape[0], w.shape[1], w.shape[1], H[hin[n]].data_ptr(),
-                                              s2w[n].data_ptr(), p.data_ptr(), c.data_ptr(), None, wgs_per_cu, sp))
+        chk("sweep", lib.nvfp4_scale_sweep_ex(w.data_ptr(), w.shape[0], w.shape[1], w.shape[1],
+                                              Hb[b][hin[n]].data_ptr(), s2wb[b][n].data_ptr(), p.data_ptr(),
+                                              c.data_ptr(), None, wgs_per_cu, sp))
 
-    def hessian_stream(s, evh):
+    def hessian_stream(s, evh, b=0):
         """The 16 chunk calls of calibration stream s, bracketed by one event
         pair (an event between calls would leave the GPU idle ~10 us each)."""
         evh[s][0].record(stream)
         for x in X[s]:
-            chk("hessian", lib.nvfp4_hessian_accum(x.data_ptr(), x.shape[0], x.shape[1], x.shape[1], H[s].data_ptr(),
-                                                   amax_x[s].data_ptr(), ws.data_ptr(), ws.numel(), sptr))
+            chk("hessian", lib.nvfp4_hessian_accum(x.data_ptr(), x.shape[0], x.shape[1], x.shape[1],
+                                                   Hb[b][s].data_ptr(), amax_xb[b][s].data_ptr(), ws.data_ptr(),
+                                                   ws.numel(), sptr))
         evh[s][1].record(stream)
 
     def step_serial(ev):
@@ -203,43 +211,46 @@ def main():
             stage_calls(k, sptr)
             ev[k].record(stream)
 
-    def step(ev):
-        """The timed step: the same work on two streams.  The second stream
-        takes a1 while the first calibration stream's Hessian starts, then
-        (once that H is done) the ALU-bound gate/up sweeps and the small
-        a4-a6 passes while the HBM-bound Hessian of the down-projection
-        stream runs; the down sweep follows on the first stream."""
+    def step(ev, b, wait_ev):
+        """The timed step, on buffer set b (H, amax and scale_2 alternate
+        between consecutive steps).  The first HIP stream accumulates both
+        calibration streams' H; the second takes a1 and a4-a6, the gate/up
+        sweeps once the first H is done and the down sweep once the second
+        is, every sweep capped at one workgroup per CU.  So the down sweep of
+        one step runs beside the next step's first Hessian; wait_ev (the
+        second stream's end of the step two back, the last reader of set b)
+        guards the reuse of set b."""
         ev["start"].record(stream)
-        side.wait_event(ev["start"])                             # the previous step is done
-        stage_calls("a1_scale2", sptr_b)
-        ev["a1_done"].record(side)
-        for s in (0, 1):
-            H[s].zero_()
-            amax_x[s].zero_()
-        hessian_stream(0, ev["h"])
-        ev["h0_done"].record(stream)
-        side.wait_event(ev["h0_done"])
-        hessian_stream(1, ev["h"])
-        for n in ("gate", "up"):
-            sweep(n, sptr_b, 1)                                  # one workgroup per CU beside the Hessian
+        stage_calls("a1_scale2", sptr_b, b)
         for k in ("a4_quantize", "a5_dequant", "a6_restore", "a6_cast"):
             stage_calls(k, sptr_b)
+        if wait_ev is not None:
+            stream.wait_event(wait_ev)
+        for s in (0, 1):
+            Hb[b][s].zero_()
+            amax_xb[b][s].zero_()
+        hessian_stream(0, ev["h"], b)
+        ev["h0_done"].record(stream)
+        side.wait_event(ev["h0_done"])
+        for n in ("gate", "up"):
+            sweep(n, sptr_b, 1, b)
+        hessian_stream(1, ev["h"], b)
+        ev["h1_done"].record(stream)
+        side.wait_event(ev["h1_done"])
+        sweep("down", sptr_b, 1, b)
         ev["side_done"].record(side)
-        stream.wait_event(ev["a1_done"])                         # scale_2 of the down weight
-        sweep("down", sptr)
-        stream.wait_event(ev["side_done"])
-        ev["end"].record(stream)
 
     def new_events(serial=False):
         E = lambda: torch.cuda.Event(enable_timing=True)
         h = [(E(), E()) for s in (0, 1)]
         if serial:
             return dict({k: E() for k in ["start"] + marks}, h=h)
-        return {"start": E(), "a1_done": E(), "h0_done": E(), "side_done": E(), "end": E(), "h": h}
+        return {"start": E(), "h0_done": E(), "h1_done": E(), "side_done": E(), "h": h}
 
     log(f"warmup {args.warmup} step(s)")
-    for _ in range(args.warmup):
-        step(new_events())
+    wev = [new_events() for _ in range(args.warmup)]
+    for i in range(args.warmup):
+        step(wev[i], i % NB, wev[i - NB]["side_done"] if i >= NB else None)
     torch.cuda.synchronize()
     fb = int(c5[2].sum().item())
 
@@ -248,23 +259,30 @@ def main():
     torch.cuda.synchronize()
     t_begin = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], i % NB, evs[i - NB]["side_done"] if i >= NB else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_begin
     ms_per_step = wall * 1e3 / args.steps
-    event_step_ms = sum(ev["start"].elapsed_time(ev["end"]) for ev in evs) / args.steps
     # mean Hessian call (partial + reduce) on its stream inside the timed steps
     h_call_ms = sum(a.elapsed_time(b) for ev in evs for a, b in ev["h"]) / (args.steps * 32)
 
     # the overlapped schedule must produce exactly what the serial order does
-    def outputs():
-        d = {"H0": H[0], "H1": H[1], "amax_x0": amax_x[0], "amax_x1": amax_x[1], "q3_packed": q3[0],
+    def outputs(b=0):
+        d = {"H0": Hb[b][0], "H1": Hb[b][1], "amax_x0": amax_xb[b][0], "amax_x1": amax_xb[b][1],
+             "s2w_gate": s2wb[b]["gate"], "s2w_up": s2wb[b]["up"], "s2w_down": s2wb[b]["down"], "q3_packed": q3[0],
              "q3_codes": q3[1], "dq3": dq3, "c5_codes": c5[0], "c5_scale2": c5[1], "c5_fallbacks": c5[2]}
         for n in W:
             d[f"{n}_packed"], d[f"{n}_codes"] = sw_out[n]
         return d
 
-    snap = {k: t.clone() for k, t in outputs().items()}
+    bl = (args.steps - 1) % NB
+    snap = {k: t.clone() for k, t in outputs(bl).items()}
+    if args.steps >= NB:
+        other = outputs(1 - bl)
+        diff2 = [k for k in ("H0", "H1", "amax_x0", "amax_x1", "s2w_gate", "s2w_up", "s2w_down")
+                 if not torch.equal(other[k], snap[k])]
+        if diff2:
+            raise RuntimeError(f"the two buffer sets differ: {diff2}")
     # per-stage times from the same work in stage order on one stream
     n_serial = max(1, min(args.steps, 5))
     evs_serial = [new_events(serial=True) for _ in range(n_serial + 1)]
@@ -337,8 +355,8 @@ def main():
         roof = {"kernel": "hessian_partial_kernel+hessian_reduce_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "per_launch": f"{x_bytes / 32 / 1e9:.4f} GB avg, {per_launch_s * 1e3:.4f} ms avg (events around "
-                              f"each calibration stream's 16 calls, on their stream, in the timed steps, where the "
-                              f"second stream's calls share the GPU with the side-stream sweeps)",
+                              f"each calibration stream's 16 calls, on their stream, in the timed steps, where they "
+                              f"share the GPU with the side-stream sweeps)",
                 "alone": {"ms_per_launch": round(h_call_serial_ms, 4), "achieved": round(alone, 1),
                           "frac": round(alone / HBM_PEAK_GBS, 4),
                           "note": "the same calls in the serial pass, with nothing else running"}}
@@ -548,11 +566,11 @@ def main():
             "calibration_tokens": datagen.C4_TOKENS,
             "chunk_tokens": datagen.C4_CHUNK,
             "parallelism": "single GPU",
-            "schedule": "timed steps: a2 of both calibration streams and the down-weight sweep on one HIP "
-                        "stream; a1 on a second stream beside the first calibration stream's Hessian, then the "
-                        "gate/up sweeps (capped at one workgroup per CU) and a4-a6 on it once that H is done "
-                        "(checked bit-exact against the serial order); stages: the same work in stage order "
-                        "on one stream",
+            "schedule": "timed steps: a2 of both calibration streams on one HIP stream; a1, a4-a6 and the three "
+                        "sweeps (capped at one workgroup per CU) on a second stream, the gate/up sweeps beside the "
+                        "second calibration stream's Hessian and the down sweep beside the next step's first "
+                        "(two alternating sets of H/amax/scale_2 buffers; checked bit-exact against the serial "
+                        "order); stages: the same work in stage order on one stream",
             "serial_step_ms": round(step_ms, 4),
         },
         "roofline": roof,
