@@ -263,9 +263,22 @@ __device__ __forceinline__ int exact_index(float ax, const float* tau) {
   return idx;
 }
 
-// Packed E2M1 nibbles of 8 values at code c on one level (element 2i in the
-// low nibble of byte i): levels 0-2 through the FP4 convert (RNE, saturating)
-// of the certified fast quotient, level 3 by the exact thresholds.
+// Packed E2M1 nibbles of 8 values (element 2i in the low nibble of byte i)
+// on fast level 0-2, given the code's table values: d, its reciprocal
+// (level 0: t.r, else t.rh) and t.rl; the FP4 convert (RNE, saturating) of
+// the certified fast quotient.
+template <int LEVEL>
+__device__ __forceinline__ uint32_t nibbles8_vals(const float* x, float d, float rh, float rl) {
+  static_assert(LEVEL >= 0 && LEVEL <= 2, "fast levels only");
+  uint32_t nb = cvt_fp4x2<0>(0u, fast_quot(x[0], d, rh, rl, LEVEL), fast_quot(x[1], d, rh, rl, LEVEL));
+  nb = cvt_fp4x2<1>(nb, fast_quot(x[2], d, rh, rl, LEVEL), fast_quot(x[3], d, rh, rl, LEVEL));
+  nb = cvt_fp4x2<2>(nb, fast_quot(x[4], d, rh, rl, LEVEL), fast_quot(x[5], d, rh, rl, LEVEL));
+  nb = cvt_fp4x2<3>(nb, fast_quot(x[6], d, rh, rl, LEVEL), fast_quot(x[7], d, rh, rl, LEVEL));
+  return nb;
+}
+
+// Packed E2M1 nibbles of 8 values at code c on one level: levels 0-2 as
+// above with the code's table values, level 3 by the exact thresholds.
 template <int LEVEL>
 __device__ __forceinline__ uint32_t nibbles8_level(const float* x, int c, const CodeTables& t) {
   if constexpr (LEVEL == 3) {
@@ -278,12 +291,7 @@ __device__ __forceinline__ uint32_t nibbles8_level(const float* x, int c, const 
     }
     return o;
   } else {
-    const float d = t.d[c], rh = LEVEL == 0 ? t.r[c] : t.rh[c], rl = t.rl[c];
-    uint32_t nb = cvt_fp4x2<0>(0u, fast_quot(x[0], d, rh, rl, LEVEL), fast_quot(x[1], d, rh, rl, LEVEL));
-    nb = cvt_fp4x2<1>(nb, fast_quot(x[2], d, rh, rl, LEVEL), fast_quot(x[3], d, rh, rl, LEVEL));
-    nb = cvt_fp4x2<2>(nb, fast_quot(x[4], d, rh, rl, LEVEL), fast_quot(x[5], d, rh, rl, LEVEL));
-    nb = cvt_fp4x2<3>(nb, fast_quot(x[6], d, rh, rl, LEVEL), fast_quot(x[7], d, rh, rl, LEVEL));
-    return nb;
+    return nibbles8_vals<LEVEL>(x, t.d[c], LEVEL == 0 ? t.r[c] : t.rh[c], t.rl[c]);
   }
 }
 

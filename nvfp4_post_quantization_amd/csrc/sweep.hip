@@ -102,10 +102,8 @@ __device__ void schur_sqrt(const float* __restrict__ Hg, int lane, float* out) {
   if (lane < 16) out[lane] = (float)sqrt(S);
 }
 
-// e = w - q d for the 16 elements at code c (lane-varying), exact quantization.
-__device__ __forceinline__ void block_error(const float* wv, int c, const CodeTables& t, int mode, float* e) {
-  const float d = t.d[c];
-  const uint2 nb = nibbles16(wv, c, t, mode);
+// e = w - q d for the 16 elements from their nibbles nb at block scale d.
+__device__ __forceinline__ void error_from_nibbles(const float* wv, uint2 nb, float d, float* e) {
   float q[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -117,6 +115,11 @@ __device__ __forceinline__ void block_error(const float* wv, int c, const CodeTa
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) e[i] = fmaf(-q[i], d, wv[i]);
+}
+
+// e = w - q d for the 16 elements at code c (lane-varying), exact quantization.
+__device__ __forceinline__ void block_error(const float* wv, int c, const CodeTables& t, int mode, float* e) {
+  error_from_nibbles(wv, nibbles16(wv, c, t, mode), t.d[c], e);
 }
 
 // e^T H e with the upper triangle of H (wave-uniform, in LDS: broadcast reads):
@@ -131,6 +134,94 @@ __device__ __forceinline__ float quad_form(const float* e, const float* Hg, cons
     acc = fmaf(e[i], v, acc);
   }
   return 2.0f * acc;
+}
+
+// The window search of one block around its max-based code c0 (code 0 and
+// c0 already evaluated into best/bestc), closing each side by its Schur
+// bound.  MODE 0 and 1 (one fast level for every code): the table values of
+// the two candidates, codes lo - 1 and hi + 1, stay in registers, and when a
+// side advances its replacement is requested from LDS at once and taken in
+// at the top of the next step, so the lookup's latency hides behind this
+// step's quantization and quadratic form.  MODE 2 (per-code levels) reads
+// the tables at each step.  Every lane computes exactly what the table reads
+// would give.
+template <int MODE>
+__device__ __forceinline__ void search_block(const float* wv, const float* a, const float* b, int c0, bool done,
+                                             float& best, int& bestc, const CodeTables& t, const float* Hg,
+                                             const float* hh, float thr_scale) {
+  // table values of code c on the mode's level: d, reciprocal (level 0: r,
+  // level 1: rh) and the reciprocal's low part (level 1 only)
+  auto rec = [&](int c) { return MODE == 0 ? t.r[c] : t.rh[c]; };
+  auto low = [&](int c) { return MODE == 1 ? t.rl[c] : 0.0f; };
+  float dl = 0.0f, ql = 0.0f, pl = 0.0f, dh = 0.0f, qh = 0.0f, ph = 0.0f;
+  float nd = 0.0f, nq = 0.0f, np = 0.0f;                    // requested replacement, not yet taken in
+  bool nlo = false, npend = false;
+  if constexpr (MODE != 2) {                                 // 1 <= c0 <= 126
+    dl = t.d[c0 - 1]; ql = rec(c0 - 1); pl = low(c0 - 1);
+    dh = t.d[c0 + 1]; qh = rec(c0 + 1); ph = low(c0 + 1);
+  }
+  int lo = c0, hi = c0, side = 0;
+  bool done_lo = false, done_hi = false;
+  while (true) {
+    if constexpr (MODE != 2) {
+      if (npend) {
+        if (nlo) { dl = nd; ql = nq; pl = np; } else { dh = nd; qh = nq; ph = np; }
+      }
+    }
+    int next = c0;
+    bool take_lo = false;
+    if (!done) {
+      const float thr = best * thr_scale;
+      if (!done_lo) {
+        if (lo <= 1) {
+          done_lo = true;
+        } else {
+          const float x = 6.0f * (MODE == 2 ? t.d[lo - 1] : dl);
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(-x, b[i], a[i]));
+          if (m * m > thr) done_lo = true;
+        }
+      }
+      if (!done_hi) {
+        if (hi >= kCodes - 1) {
+          done_hi = true;
+        } else {
+          const float qz = 0.25f * (MODE == 2 ? t.d[hi + 1] : dh);
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(wv[i]) <= qz ? a[i] : 0.0f);
+          if (m * m > thr) done_hi = true;
+        }
+      }
+      if (done_lo && done_hi) {
+        done = true;
+      } else {
+        take_lo = !done_lo && (done_hi || side == 0);
+        next = take_lo ? lo - 1 : hi + 1;
+        side ^= 1;
+      }
+    }
+    if (!__any(!done)) break;                                // wave-uniform exit; at most 126 steps
+    float e[16];
+    if constexpr (MODE == 2) {
+      block_error(wv, next, t, 2, e);
+    } else {
+      const float d = take_lo ? dl : dh, q = take_lo ? ql : qh, p = take_lo ? pl : ph;
+      // the replacement for the side that advances (1 <= next <= 126, so in bounds)
+      const int nc = take_lo ? next - 1 : next + 1;
+      nd = t.d[nc]; nq = rec(nc); np = low(nc);
+      nlo = take_lo;
+      npend = true;
+      error_from_nibbles(wv, make_uint2(nibbles8_vals<MODE>(wv, d, q, p), nibbles8_vals<MODE>(wv + 8, d, q, p)),
+                         d, e);
+    }
+    const float cc = quad_form(e, Hg, hh);
+    if (!done) {
+      if (next < lo) lo = next; else hi = next;
+      if (cc < best || (cc == best && next < bestc)) { best = cc; bestc = next; }
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t k,
@@ -204,50 +295,12 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
       const float cc = quad_form(e, Hg, hh);
       if (!done && cc < best) { best = cc; bestc = c0; }      // c0 > 0: a tie keeps code 0
     }
-    int lo = c0, hi = c0, side = 0;
-    bool done_lo = false, done_hi = false;
-    while (true) {
-      int next = c0;
-      if (!done) {
-        const float thr = best * thr_scale;
-        if (!done_lo) {
-          if (lo <= 1) {
-            done_lo = true;
-          } else {
-            const float x = 6.0f * t.d[lo - 1];
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(-x, b[i], a[i]));
-            if (m * m > thr) done_lo = true;
-          }
-        }
-        if (!done_hi) {
-          if (hi >= kCodes - 1) {
-            done_hi = true;
-          } else {
-            const float qz = 0.25f * t.d[hi + 1];
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(wv[i]) <= qz ? a[i] : 0.0f);
-            if (m * m > thr) done_hi = true;
-          }
-        }
-        if (done_lo && done_hi) {
-          done = true;
-        } else {
-          const bool take_lo = !done_lo && (done_hi || side == 0);
-          next = take_lo ? lo - 1 : hi + 1;
-          side ^= 1;
-        }
-      }
-      if (!__any(!done)) break;                              // wave-uniform exit; at most 126 steps
-      float e[16];
-      block_error(wv, next, t, mode, e);
-      const float cc = quad_form(e, Hg, hh);
-      if (!done) {
-        if (next < lo) lo = next; else hi = next;
-        if (cc < best || (cc == best && next < bestc)) { best = cc; bestc = next; }
-      }
+    if (mode == 0) {
+      search_block<0>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale);
+    } else if (mode == 1) {
+      search_block<1>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale);
+    } else {
+      search_block<2>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale);
     }
     if (valid) {
       const uint2 nb = nibbles16(wv, bestc, t, mode);
