@@ -28,15 +28,18 @@
 //  * a workgroup = 4 waves = 4 adjacent groups; lane l of wave w handles rows
 //    r0 + l (+64, ...) of group 4*blockIdx.x + w, so the four waves read each
 //    row's 128 contiguous bytes together, and H_g is uniform per wave (staged
-//    in LDS and read with broadcast loads, which run beside the VALU);
+//    in LDS once; the compiler keeps its upper triangle in VGPRs for the
+//    step loop);
 //  * per step every lane evaluates one code of its own block: E2M1
 //    quantization by the certified FP4-convert paths (nvfp4_device.hpp), then
 //    the symmetric quadratic form 2 * sum_i e_i (H_ii e_i / 2 + sum_{j>i}
-//    H_ij e_j) in fp32 (152 VALU ops);
+//    H_ij e_j) in fp32 (152 VALU ops); the table values of the two candidate
+//    codes are held in registers and fetched one step ahead;
 //  * the wave steps until all its lanes are done (lanes that finish early
 //    idle); the nibbles are re-quantized at the chosen code.
-//  * two workgroups per CU (launch bounds): the step loop fits 256 VGPRs;
-//    only the one-time table set-up spills a few values to scratch.
+//  * two workgroups per CU (launch bounds): 246 VGPRs, no scratch.  The
+//    occupancy-capped launch (one workgroup per CU, for running beside
+//    another kernel) reserves dynamic LDS so that a second one cannot fit.
 // fp32 MFMA and fp32 VALU share one datapath on this chip (measured: their
 // times add), so a dense MFMA product would not be cheaper than the
 // symmetric VALU form; pruning is what removes work.
