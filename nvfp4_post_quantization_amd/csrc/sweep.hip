@@ -37,7 +37,7 @@
 //    codes are held in registers and fetched one step ahead;
 //  * the wave steps until all its lanes are done (lanes that finish early
 //    idle); the nibbles are re-quantized at the chosen code.
-//  * two workgroups per CU (launch bounds): 246 VGPRs, no scratch.  The
+//  * two workgroups per CU (launch bounds): 248 VGPRs, no scratch.  The
 //    occupancy-capped launch (one workgroup per CU, for running beside
 //    another kernel) reserves dynamic LDS so that a second one cannot fit.
 // fp32 MFMA and fp32 VALU share one datapath on this chip (measured: their
@@ -165,47 +165,36 @@ __device__ __forceinline__ void search_block(const float* wv, const float* a, co
   }
   int lo = c0, hi = c0, side = 0;
   bool done_lo = false, done_hi = false;
+  // Branch-free steps (selects instead of divergent ifs: the exec-mask
+  // bookkeeping of nested ifs cost more issue slots than the bounds do).
   while (true) {
     if constexpr (MODE != 2) {
-      if (npend) {
-        if (nlo) { dl = nd; ql = nq; pl = np; } else { dh = nd; qh = nq; ph = np; }
-      }
+      const bool in_lo = npend && nlo, in_hi = npend && !nlo;
+      dl = in_lo ? nd : dl; ql = in_lo ? nq : ql; pl = in_lo ? np : pl;
+      dh = in_hi ? nd : dh; qh = in_hi ? nq : qh; ph = in_hi ? np : ph;
     }
-    int next = c0;
-    bool take_lo = false;
-    if (!done) {
-      const float thr = best * thr_scale;
-      if (!done_lo) {
-        if (lo <= 1) {
-          done_lo = true;
-        } else {
-          const float x = 6.0f * (MODE == 2 ? t.d[lo - 1] : dl);
-          float m = 0.0f;
+    // both bounds for every lane (1 <= lo and hi <= 126, so the reads are
+    // in bounds; a side already closed, or at the end of the range, ignores
+    // its value)
+    const float dlo = MODE == 2 ? t.d[lo - 1] : dl;
+    const float dhi = MODE == 2 ? t.d[hi + 1] : dh;
+    const float thr = best * thr_scale;
+    const float x = 6.0f * dlo, qz = 0.25f * dhi;
+    float mlo = 0.0f, mhi = 0.0f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(-x, b[i], a[i]));
-          if (m * m > thr) done_lo = true;
-        }
-      }
-      if (!done_hi) {
-        if (hi >= kCodes - 1) {
-          done_hi = true;
-        } else {
-          const float qz = 0.25f * (MODE == 2 ? t.d[hi + 1] : dh);
-          float m = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(wv[i]) <= qz ? a[i] : 0.0f);
-          if (m * m > thr) done_hi = true;
-        }
-      }
-      if (done_lo && done_hi) {
-        done = true;
-      } else {
-        take_lo = !done_lo && (done_hi || side == 0);
-        next = take_lo ? lo - 1 : hi + 1;
-        side ^= 1;
-      }
+    for (int i = 0; i < 16; ++i) {
+      mlo = fmaxf(mlo, fmaf(-x, b[i], a[i]));
+      mhi = fmaxf(mhi, fabsf(wv[i]) <= qz ? a[i] : 0.0f);
     }
-    if (!__any(!done)) break;                                // wave-uniform exit; at most 126 steps
+    const bool act = !done;
+    done_lo = done_lo || (act && (lo <= 1 || mlo * mlo > thr));
+    done_hi = done_hi || (act && (hi >= kCodes - 1 || mhi * mhi > thr));
+    const bool cont = act && !(done_lo && done_hi);
+    done = !cont;
+    const bool take_lo = cont && !done_lo && (done_hi || side == 0);
+    const int next = cont ? (take_lo ? lo - 1 : hi + 1) : c0;
+    side ^= cont ? 1 : 0;
+    if (!__any(cont)) break;                                 // wave-uniform exit; at most 126 steps
     float e[16];
     if constexpr (MODE == 2) {
       block_error(wv, next, t, 2, e);
@@ -220,10 +209,11 @@ __device__ __forceinline__ void search_block(const float* wv, const float* a, co
                          d, e);
     }
     const float cc = quad_form(e, Hg, hh);
-    if (!done) {
-      if (next < lo) lo = next; else hi = next;
-      if (cc < best || (cc == best && next < bestc)) { best = cc; bestc = next; }
-    }
+    lo = (cont && take_lo) ? next : lo;
+    hi = (cont && !take_lo) ? next : hi;
+    const bool better = cont && (cc < best || (cc == best && next < bestc));
+    best = better ? cc : best;
+    bestc = better ? next : bestc;
   }
 }
 
