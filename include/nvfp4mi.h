@@ -339,7 +339,10 @@ size_t nvfp4_quantlinear_workspace_bytes(int64_t tokens, int64_t k);
  * fake QDQ is one kernel of this library into the workspace; the product is
  * a plain bf16 GEMM through hipBLASLt (fp32 compute; its summation order is
  * hipBLASLt's).  The first call on a device creates a hipBLASLt handle (kept
- * until the process ends); each new shape runs one algorithm query.
+ * until the process ends).  The first call for each new shape times up to 16
+ * of hipBLASLt's candidate algorithms on `stream` and keeps the fastest, so
+ * that call synchronises the stream; under graph capture it takes the first
+ * candidate untimed.
  * x [tokens][ldx] bf16; w [out_features][ldw] bf16; y [tokens][ldy] bf16;
  * rows 16-byte aligned.  workspace: 256-byte aligned device buffer of at
  * least nvfp4_quantlinear_workspace_bytes(tokens, k) bytes (scratch).

@@ -11,6 +11,10 @@
 // it would be recomputed for every output tile (out_features / tile times).
 // The product is a plain bf16 GEMM, so it goes to hipBLASLt (TN layout:
 // y^T [O, T] = wh [O, K] * xh^T [K, T] in column-major terms), fp32 compute.
+// The first call for a shape on a device takes up to kTuneAlgos of
+// hipBLASLt's heuristic candidates, times each on the caller's stream (so
+// that call synchronises it) and keeps the fastest; a stream under graph
+// capture takes the first candidate untimed instead.
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -25,6 +29,8 @@ namespace {
 
 constexpr size_t kGemmWorkspace = 32u << 20;       // hipBLASLt workspace, carved from the caller's buffer
 constexpr size_t kAlign = 256;
+constexpr int kTuneAlgos = 16;                       // heuristic candidates timed at the first call of a shape
+constexpr int kTuneReps = 2;                         // timed runs per candidate (after one warm run)
 
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -52,6 +58,48 @@ struct Layouts {
     if (desc) hipblasLtMatmulDescDestroy(desc);
   }
 };
+
+// Time each candidate (one warm run, then kTuneReps runs between two events)
+// and return the index of the fastest that ran; candidates that fail to run
+// are skipped.  Writes y (with correct results) along the way.
+int tune(hipblasLtHandle_t handle, const Layouts& L, const hipblasLtMatmulHeuristicResult_t* heur, int n,
+         const void* w, const void* xh, void* y, void* ws, hipStream_t s, int* pick) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t he = hipEventCreate(&e0);
+  if (he == hipSuccess) he = hipEventCreate(&e1);
+  if (he != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    set_hip_error(he, "hipEventCreate");
+    return NVFP4_ERR_HIP;
+  }
+  const float alpha = 1.0f, beta = 0.0f;
+  float best = 0.0f;
+  int found = -1;
+  int st = NVFP4_OK;
+  for (int i = 0; i < n && st == NVFP4_OK; ++i) {
+    if (heur[i].state != HIPBLAS_STATUS_SUCCESS || heur[i].workspaceSize > kGemmWorkspace) continue;
+    auto run = [&]() {
+      return hipblasLtMatmul(handle, L.desc, &alpha, w, L.a, xh, L.b, &beta, y, L.c, y, L.c, &heur[i].algo, ws,
+                             kGemmWorkspace, s);
+    };
+    if (run() != HIPBLAS_STATUS_SUCCESS) continue;
+    bool ok = hipEventRecord(e0, s) == hipSuccess;
+    for (int r = 0; r < kTuneReps && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
+    he = hipEventRecord(e1, s);
+    if (he == hipSuccess) he = hipEventSynchronize(e1);
+    if (he != hipSuccess) { set_hip_error(he, "tuning the GEMM"); st = NVFP4_ERR_HIP; break; }
+    float ms = 0.0f;
+    if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (found < 0 || ms < best)) {
+      best = ms;
+      found = i;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st) return st;
+  *pick = found < 0 ? 0 : found;
+  return NVFP4_OK;
+}
 
 }  // namespace
 
@@ -102,13 +150,19 @@ int launch_quantlinear(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx
       if ((st = blas_status(hipblasLtMatmulPreferenceCreate(&pref), "PreferenceCreate"))) return st;
       const uint64_t wsb = kGemmWorkspace;
       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof wsb);
-      hipblasLtMatmulHeuristicResult_t heur[1];
+      hipblasLtMatmulHeuristicResult_t heur[kTuneAlgos];
       int n = 0;
-      hipblasStatus_t hs = hipblasLtMatmulAlgoGetHeuristic(handle, L.desc, L.a, L.b, L.c, L.c, pref, 1, heur, &n);
+      hipblasStatus_t hs =
+          hipblasLtMatmulAlgoGetHeuristic(handle, L.desc, L.a, L.b, L.c, L.c, pref, kTuneAlgos, heur, &n);
       hipblasLtMatmulPreferenceDestroy(pref);
       if ((st = blas_status(hs, "AlgoGetHeuristic"))) return st;
       if (n < 1) { set_error_text("hipBLASLt: no algorithm for this GEMM"); return NVFP4_ERR_HIP; }
-      it = G.algos.emplace(key, heur[0].algo).first;
+      int pick = 0;
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (n > 1 && hipStreamIsCapturing(s, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+        if ((st = tune(handle, L, heur, n, w, xh, y, gemm_ws, s, &pick))) return st;
+      }
+      it = G.algos.emplace(key, heur[pick].algo).first;
     }
     algo = it->second;
   }
