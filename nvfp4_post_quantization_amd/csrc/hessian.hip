@@ -314,6 +314,11 @@ __global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint
                                                                        int64_t slabs, int64_t streams,
                                                                        float* __restrict__ ws, float* amax) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
+  // Beside a VALU-bound kernel on another stream (a sweep) this kernel's
+  // waves win instruction arbitration: the memory stream is what bounds it,
+  // and a pure-FMA kernel at one wave per SIMD slowed it by half at the
+  // default priority, by 2% at this one.  Alone it changes nothing.
+  __builtin_amdgcn_s_setprio(3);
   const FqState q{};
   const u16x2 amx = partial_body<-1>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws,
                                      amax != nullptr, tile, q);
