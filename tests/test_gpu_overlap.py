@@ -82,3 +82,21 @@ def test_sweeps_beside_hessian_on_another_stream():
     assert torch.equal(H1, H1_ref)
     for n in W:
         assert _equal(out[n], sw_ref[n]), n
+
+
+@pytest.mark.parametrize("rows,k", [(1, 16), (65, 48), (333, 272), (130, 4096)])
+def test_capped_sweep_ragged(rows, k):
+    """Row counts off the 64-row blocks and narrow or single-group widths:
+    the capped launch gives the uncapped outputs, costs included."""
+    note(f"capped sweep rows={rows} k={k}")
+    rng = np.random.default_rng(rows * 7 + k)
+    w = datagen.f32_to_bf16_bits(rng.normal(0.0, 0.02, (rows, k)).astype(np.float32))
+    x = datagen.f32_to_bf16_bits(rng.laplace(0.0, 1.0, (256, k)).astype(np.float32))
+    h32 = N.hessian(x).astype(np.float32)
+    wd = to_dev_bf16(w)
+    H = torch.from_numpy(h32).to(DEV)
+    s2, _ = nq.compute_scale2(wd)
+    ref = nq.scale_sweep(wd, H, s2, want_cost=True)
+    cap = nq.scale_sweep(wd, H, s2, want_cost=True, wgs_per_cu=1)
+    assert _equal(ref, cap)
+    compare_sweep(w, h32, float(host(s2)[0]), host(cap[0]), host(cap[1]), host(cap[2]))
