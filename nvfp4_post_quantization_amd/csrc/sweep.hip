@@ -45,6 +45,8 @@
 // symmetric VALU form; pruning is what removes work.
 // H is taken as symmetric (its upper triangle is used), as the accumulate
 // entry point produces it.
+#include <mutex>
+
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -310,26 +312,34 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
 
 }  // namespace
 
-// LDS to reserve per workgroup so that at most one sweep workgroup fits on a
-// CU: half the CU's LDS plus 1 KiB, less what the kernel declares.  The rest
-// of the CU (just under half its LDS, and 272 of 512 VGPRs per SIMD beside
-// the sweep's one wave) stays free for a kernel on another stream.
-static int query_one_per_cu_lds() {
-  int dev = 0, lds_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
-  hipFuncAttributes fa;
-  if (e == hipSuccess) e = hipFuncGetAttributes(&fa, (const void*)sweep_kernel);
-  const int want = lds_cu / 2 + 1024 - (int)fa.sharedSizeBytes;
-  if (e == hipSuccess) e = hipFuncSetAttribute((const void*)sweep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
-  if (e != hipSuccess) { set_hip_error(e, "sweep LDS reservation"); return -1; }
-  return want;
-}
+// The capped launch reserves, per workgroup, half the CU's LDS plus 1 KiB
+// less what the kernel declares, so that at most one sweep workgroup fits on
+// a CU; the rest of the CU (just under half its LDS, and about 260 of 512
+// VGPRs per SIMD beside the sweep's one wave) stays free for a kernel on
+// another stream.  The size is found and the kernel's limit raised once per
+// device, at that device's first capped launch (0 = not done yet).
+static std::mutex g_lds_mu;
+static int g_lds_want[64] = {};
 
 static int one_per_cu_lds(unsigned* dyn) {
-  static const int want = query_one_per_cu_lds();          // once per process (thread-safe initialisation)
-  if (want < 0) return NVFP4_ERR_HIP;
-  *dyn = (unsigned)want;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { set_hip_error(e, "hipGetDevice"); return NVFP4_ERR_HIP; }
+  if (dev < 0 || dev >= 64) return NVFP4_ERR_BAD_INPUT;
+  std::lock_guard<std::mutex> lock(g_lds_mu);
+  if (g_lds_want[dev] == 0) {
+    int lds_cu = 0;
+    hipFuncAttributes fa;
+    e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess) e = hipFuncGetAttributes(&fa, (const void*)sweep_kernel);
+    if (e == hipSuccess) {
+      const int want = lds_cu / 2 + 1024 - (int)fa.sharedSizeBytes;
+      e = hipFuncSetAttribute((const void*)sweep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+      if (e == hipSuccess) g_lds_want[dev] = want;
+    }
+    if (e != hipSuccess) { set_hip_error(e, "sweep LDS reservation"); return NVFP4_ERR_HIP; }
+  }
+  *dyn = (unsigned)g_lds_want[dev];
   return NVFP4_OK;
 }
 
