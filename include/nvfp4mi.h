@@ -173,10 +173,12 @@ int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw,
  * calibration stream).  wgs_per_cu = 0: as nvfp4_scale_sweep (as many
  * workgroups per CU as fit); 1: at most one sweep workgroup per CU, by
  * reserving just over half of the CU's LDS per workgroup, which leaves the
- * rest of the LDS and 272 VGPRs per SIMD to the other kernel.  Results are
- * identical to nvfp4_scale_sweep's.  The reservation is sized once per
- * process for the current device.
- * Errors: as nvfp4_scale_sweep, plus BAD_INPUT (wgs_per_cu not 0 or 1).
+ * rest of the LDS and about 260 VGPRs per SIMD to the other kernel.  Results
+ * are identical to nvfp4_scale_sweep's.  The reservation is sized, and the
+ * kernel's dynamic-LDS limit raised, once per device at its first capped call
+ * (thread-safe).
+ * Errors: as nvfp4_scale_sweep, plus BAD_INPUT (wgs_per_cu not 0 or 1, or a
+ *         device index of 64 or more when capped).
  */
 int nvfp4_scale_sweep_ex(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw,
                          const float* H, const float* scale2, uint8_t* packed,
