@@ -45,7 +45,8 @@ def test_capped_sweep_equals_uncapped_config2():
 
 def test_sweeps_beside_hessian_on_another_stream():
     """Two 65536-token K = 12288 chunks accumulate on one stream while the
-    gate and up weights are swept, capped, on a second stream."""
+    gate and up weights are swept, capped, on a second stream; then the down
+    weight is swept, capped, beside two K = 4096 chunks."""
     note("capped sweeps beside the Hessian")
     W = {n: to_dev_bf16(datagen.config4_weights(n)) for n in ("gate", "up")}
     x0 = datagen.config4_chunk_torch(0, 0, DEV)
@@ -54,7 +55,7 @@ def test_sweeps_beside_hessian_on_another_stream():
     del x0
     X1 = [datagen.config4_chunk_torch(1, c, DEV) for c in range(2)]
     s2 = {n: nq.compute_scale2(w)[0] for n, w in W.items()}
-    ws = torch.empty(nq.hessian_workspace_bytes(65536, 12288), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(nq.hessian_workspace_bytes(65536, k) for k in (4096, 12288)), dtype=torch.uint8, device=DEV)
 
     # alone, one after the other
     H1_ref = torch.zeros((768, 16, 16), dtype=torch.float32, device=DEV)
@@ -82,6 +83,33 @@ def test_sweeps_beside_hessian_on_another_stream():
     assert torch.equal(H1, H1_ref)
     for n in W:
         assert _equal(out[n], sw_ref[n]), n
+
+    # as in the pipelined step: the down weight's capped sweep (under the
+    # second stream's H) on the side stream while the first stream's H of
+    # the next step accumulates into a fresh buffer
+    del X1
+    wd = to_dev_bf16(datagen.config4_weights("down"))
+    s2d = nq.compute_scale2(wd)[0]
+    down_ref = nq.scale_sweep(wd, H1_ref, s2d, want_cost=True)
+    X0 = [datagen.config4_chunk_torch(0, c, DEV) for c in range(2)]
+    H0_ref = torch.zeros_like(H0)
+    for x in X0:
+        nq.hessian_accum(x, H0_ref, workspace=ws)
+    torch.cuda.synchronize()
+    H0b = torch.zeros_like(H0)
+    down = tuple(torch.empty_like(t) for t in down_ref)
+    ready = torch.cuda.Event()
+    ready.record(main)
+    side.wait_event(ready)
+    nq.scale_sweep(wd, H1_ref, s2d, want_cost=True, out=down, wgs_per_cu=1, stream=side)
+    for x in X0:
+        nq.hessian_accum(x, H0b, workspace=ws)
+    done = torch.cuda.Event()
+    done.record(side)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    assert torch.equal(H0b, H0_ref)
+    assert _equal(down, down_ref)
 
 
 @pytest.mark.parametrize("rows,k", [(1, 16), (65, 48), (333, 272), (130, 4096)])
