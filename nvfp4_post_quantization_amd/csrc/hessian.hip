@@ -13,9 +13,9 @@
 //    v_mfma_f32_16x16x32_bf16.  In that instruction lane l supplies row l%16
 //    of A and column l%16 of B for K-slots 8*(l/16)..+7; for A = X_g^T and
 //    B = X_g both are "channel l%16 at 8 tokens", so one register feeds both
-//    operands.  The lane reads its 8 tokens of one channel from LDS; the
-//    16-byte chunks are XOR-swizzled by row so the four lane groups of a read
-//    hit disjoint banks;
+//    operands.  The lane's 8 tokens of one channel come from LDS by two
+//    transposing reads (ds_read_b64_tr_b16); the 16-byte chunks are
+//    XOR-swizzled by row so the lane groups of a read hit disjoint banks;
 //  * a workgroup writes one fp32 partial per slab its range touches (at most
 //    a few); a second kernel adds, per group, the partials of that slab's
 //    workgroups to H in fp64, in workgroup order (deterministic).
@@ -230,35 +230,24 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
 #pragma unroll
       for (int gsub = 0; gsub < 2; ++gsub) {
         const int gl = 2 * wave + gsub;               // group within the slab
-        const int col = gl * 16 + ch;                 // column within the slab
-        const int j = col >> 3, within = col & 7;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          u16x8 v;
-          if constexpr (QM >= 0) {
-            // fake-quant kernel (ALU-heavier: measured 5-10% faster this way):
-            // two transposing reads; lane jj of each 16-lane group fetches 4
-            // channels (4*(jj&3)..+3 of the group) of token R0 + jj/4, and
-            // after the transpose lane ch holds its channel at 4 consecutive
-            // tokens, the same 8 values in the same order as the plain reads
-            const int jj = lane & 15;
-            const int c4 = gl * 16 + 4 * (jj & 3);
-            const int R0 = 32 * m + 8 * q + (jj >> 2);
-            const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)&tile[R0 * kSlabCols + swz(c4 >> 3, R0) * 8 + (c4 & 7)]);
-            const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)&tile[(R0 + 4) * kSlabCols + swz(c4 >> 3, R0 + 4) * 8 +
-                                                                (c4 & 7)]);
-            v = __builtin_bit_cast(u16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-          } else {
-            // plain kernel: 2-byte reads (the transposing reads measured 2%
-            // slower at K = 12288 here)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int R = 32 * m + 8 * q + e;
-              v[e] = tile[R * kSlabCols + swz(j, R) * 8 + within];
-            }
-          }
+          // Two transposing reads: lane jj of each 16-lane group fetches 4
+          // channels (4*(jj&3)..+3 of the group) of token R0 + jj/4, and after
+          // the transpose lane ch holds its channel at 4 consecutive tokens:
+          // rows 32m + 8q .. +7 of column 16 gl + ch, in order.  (Against eight 2-byte
+          // reads: 5-10% faster in the fake-quant kernel; in the plain kernel
+          // equal alone and 0.8% faster per benchmark step beside the sweeps,
+          // from fewer instructions per tile.)
+          const int jj = lane & 15;
+          const int c4 = gl * 16 + 4 * (jj & 3);
+          const int R0 = 32 * m + 8 * q + (jj >> 2);
+          const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)&tile[R0 * kSlabCols + swz(c4 >> 3, R0) * 8 + (c4 & 7)]);
+          const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)&tile[(R0 + 4) * kSlabCols + swz(c4 >> 3, R0 + 4) * 8 +
+                                                              (c4 & 7)]);
+          const u16x8 v = __builtin_bit_cast(u16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
           if (QM < 0 && want_amax) {
             const u32x4 d = __builtin_bit_cast(u32x4, v);
             amx = abs_max2(abs_max2(abs_max2(abs_max2(amx, d.x), d.y), d.z), d.w);
