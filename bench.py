@@ -336,7 +336,7 @@ def main():
                      TFLOPs=round(tf, 2), frac_fp32_peak=round(tf / FP32_PEAK_TFLOPS, 4))
         stage_rep[k] = d
     stage_rep["a3_sweep"]["note"] = ("algorithmic flops count all 127 codes of every block; the pruned search "
-                                     "evaluates about 14 per block, so this fraction is not a VALU utilisation")
+                                     "evaluates about 15 per block, so this fraction is not a VALU utilisation")
     stage_rep["a6_cast"]["fallback_mx_blocks"] = fb
     stage_rep["a6_cast"]["forced_by_generator"] = n_forced
     stage_rep["a6_cast"]["input_restore_ms"] = round(st_ms["a6_restore"], 4)   # in the step, not in this stage
