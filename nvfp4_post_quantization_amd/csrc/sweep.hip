@@ -35,6 +35,13 @@
 //    the symmetric quadratic form 2 * sum_i e_i (H_ii e_i / 2 + sum_{j>i}
 //    H_ij e_j) in fp32 (152 VALU ops); the table values of the two candidate
 //    codes are held in registers and fetched one step ahead;
+//  * a diagonal screen comes first: when H_g's unit-diagonal scaling has
+//    Gershgorin row sums r_i <= 0.9, e^T H e >= (1 - max r) sum_i H_ii e_i^2,
+//    and a wave whose searching lanes all have that bound above the
+//    threshold skips the form for this step (on the MLP calibration
+//    workload about half the steps; 32 extra ops per step).  Codes it skips
+//    could not have won, so the outputs are those of the unscreened search,
+//    bit for bit;
 //  * the wave steps until all its lanes are done (lanes that finish early
 //    idle); the nibbles are re-quantized at the chosen code.
 //  * two workgroups per CU (launch bounds): 248 VGPRs, no scratch.  The
@@ -145,6 +152,38 @@ __device__ __forceinline__ float quad_form(const float* e, const float* Hg, cons
   return 2.0f * acc;
 }
 
+// Factor of the diagonal screen for group H_g (every lane returns it; 0 =
+// screen off).  With r_i = sum_{j != i} |H_ij| / sqrt(H_ii H_jj) (upper
+// triangle mirrored), Gershgorin's theorem on the unit-diagonal scaling of H
+// gives e^T H e >= (1 - max_i r_i) sum_i H_ii e_i^2.  The screen is used only
+// when max_i r_i <= 0.9: then the fp32 quadratic form's relative rounding
+// error stays below 2e-5 (its absolute terms sum to at most (1 + r)/(1 - r)
+// times its value), well inside the 1e-4 margin taken here plus the pruning
+// margin, so a screened-out code is one whose computed cost exceeds the best.
+// Returns 2 (1 - max r)(1 - 1e-4), the factor of sum_i e_i (H_ii / 2) e_i.
+__device__ float screen_factor(const float* Hg, int lane) {
+  const int i = lane & 15;
+  const double hii = (double)Hg[i * 17];
+  double r = 0.0;
+  bool ok = hii > 0.0 && hii < 1e300;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const double hjj = (double)Hg[j * 17];
+    ok = ok && hjj > 0.0 && hjj < 1e300;
+    const double hij = (double)Hg[j < i ? j * 16 + i : i * 16 + j];
+    r += (j != i && ok) ? fabs(hij) / sqrt(hii * hjj) : 0.0;
+  }
+  ok = ok && r <= 0.9;                                       // false for NaN too
+  double rmax = 0.0;
+  bool all_ok = true;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    rmax = fmax(rmax, bcast(r, j));
+    all_ok = all_ok && __builtin_amdgcn_readlane((int)ok, j) != 0;
+  }
+  return all_ok ? (float)(2.0 * (1.0 - rmax) * (1.0 - 1e-4)) : 0.0f;
+}
+
 // The window search of one block around its max-based code c0 (code 0 and
 // c0 already evaluated into best/bestc), closing each side by its Schur
 // bound.  MODE 0 and 1 (one fast level for every code): the table values of
@@ -157,7 +196,7 @@ __device__ __forceinline__ float quad_form(const float* e, const float* Hg, cons
 template <int MODE>
 __device__ __forceinline__ void search_block(const float* wv, const float* a, const float* b, int c0, bool done,
                                              float& best, int& bestc, const CodeTables& t, const float* Hg,
-                                             const float* hh, float thr_scale) {
+                                             const float* hh, float thr_scale, float mu2) {
   // table values of code c on the mode's level: d, reciprocal (level 0: r,
   // level 1: rh) and the reciprocal's low part (level 1 only)
   auto rec = [&](int c) { return MODE == 0 ? t.r[c] : t.rh[c]; };
@@ -214,7 +253,23 @@ __device__ __forceinline__ void search_block(const float* wv, const float* a, co
       error_from_nibbles(wv, make_uint2(nibbles8_vals<MODE>(wv, d, q, p), nibbles8_vals<MODE>(wv + 8, d, q, p)),
                          d, e);
     }
-    const float cc = quad_form(e, Hg, hh);
+    // Diagonal screen (mu2 > 0, wave-uniform): the full form is skipped when
+    // no searching lane's diagonal bound mu2 * sum_i H_ii e_i^2 / 2 stays
+    // within the threshold; the forms that are computed are unchanged.
+    float cc;
+    if (mu2 > 0.0f) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s = fmaf(e[i] * e[i], hh[i], s);
+      const bool need = cont && !(mu2 * s > thr);
+      if (__any(need)) {
+        cc = quad_form(e, Hg, hh);
+      } else {
+        cc = __builtin_inff();
+      }
+    } else {
+      cc = quad_form(e, Hg, hh);
+    }
     lo = (cont && take_lo) ? next : lo;
     hi = (cont && !take_lo) ? next : hi;
     const bool better = cont && (cc < best || (cc == best && next < bestc));
@@ -257,6 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
     b[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sqS[wave][i])));
   }
   const float thr_scale = 1.0f + kPruneMargin;
+  const float mu2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(screen_factor(Hg, lane))));
 
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
   int64_t r1 = r0 + rows_per_wg;
@@ -295,11 +351,11 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
       if (!done && cc < best) { best = cc; bestc = c0; }      // c0 > 0: a tie keeps code 0
     }
     if (mode == 0) {
-      search_block<0>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale);
+      search_block<0>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale, mu2);
     } else if (mode == 1) {
-      search_block<1>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale);
+      search_block<1>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale, mu2);
     } else {
-      search_block<2>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale);
+      search_block<2>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale, mu2);
     }
     if (valid) {
       const uint2 nb = nibbles16(wv, bestc, t, mode);

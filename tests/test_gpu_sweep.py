@@ -107,6 +107,35 @@ def test_sweep_special_hessians():
     check_sweep(w, hs, s2)
 
 
+def _scaled_correlation(c, rng, groups):
+    """H_g = D C D with C unit-diagonal and D spanning 1 .. 40 (outlier channels)."""
+    d = np.exp(rng.uniform(0.0, np.log(40.0), (groups, 16)))
+    return (d[:, :, None] * c * d[:, None, :]).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind,rho", [("equi", 0.05), ("equi", 0.059), ("equi", 0.07), ("equi", 0.5),
+                                      ("signed", 0.85), ("signed", 0.95)])
+def test_sweep_correlated_hessians(kind, rho):
+    """Row sums of |C_ij| (j != i) of 15 rho ("equi") or exactly rho with random
+    signs ("signed"), below and above 0.9: the sweep's diagonal screen is on
+    for the first and off for the others; every case meets the oracle bar."""
+    note(f"sweep correlated H {kind} {rho}")
+    rng = np.random.default_rng(int(rho * 1000) + (7 if kind == "signed" else 0))
+    groups = 8
+    if kind == "equi":
+        c = np.broadcast_to((1.0 - rho) * np.eye(16) + rho * np.ones((16, 16)), (groups, 16, 16))
+    else:
+        a = rng.uniform(0.1, 1.0, (groups, 16, 16)) * rng.choice([-1.0, 1.0], (groups, 16, 16))
+        a = np.triu(a, 1)
+        a = a + np.swapaxes(a, 1, 2)
+        a *= rho / np.abs(a).sum(axis=2).max(axis=1)[:, None, None]
+        c = np.eye(16) + a
+    h = _scaled_correlation(c, rng, groups)
+    w = datagen.f32_to_bf16_bits(rng.laplace(0.0, 0.02, (320, groups * 16)).astype(np.float32))
+    _, s2 = N.tensor_scale(w)
+    check_sweep(w, h, s2)
+
+
 def test_sweep_exact_and_zero_blocks(path):
     note(f"sweep exact/zero blocks ({path})")
     s2 = 2.0 ** -10
