@@ -81,15 +81,20 @@ __device__ __forceinline__ void fp4x2_to_f32(uint32_t src, float& a, float& b) {
   a = v.x; b = v.y;
 }
 
+// The low part x * rl of a two-float quotient, clamped to the finite range
+// (one v_med3).  |rl| <= 2^-24 |rh|, so x * rl overflows only when |x * rh|
+// exceeds 2^24 times the largest float; the fma then still overflows, or
+// stays far above the E2M1 range, with the sign of x, and the quotient
+// saturates as it should, whatever the sign of rl.  Finite values pass
+// unchanged.
+__device__ __forceinline__ float quot_low(float x, float rl) {
+  return __builtin_amdgcn_fmed3f(x * rl, -3.40282347e38f, 3.40282347e38f);
+}
+
 // Level-1 quotient: x / d from the two-float reciprocal (rh + rl ~ 1/d),
-// moved one ulp toward the exact quotient when it is not exact.  The low part
-// x * rl can only overflow when x * rh does too; it is then dropped, so the
-// infinite quotient keeps the sign of x (and saturates) instead of taking the
-// sign of rl.
+// moved one ulp toward the exact quotient when it is not exact.
 __device__ __forceinline__ float quot1(float x, float d, float rh, float rl) {
-  float lo = x * rl;
-  lo = __builtin_isfinite(lo) ? lo : 0.0f;
-  const float y = __builtin_fmaf(x, rh, lo);
+  const float y = __builtin_fmaf(x, rh, quot_low(x, rl));
   const float rho = __builtin_fmaf(-y, d, x);            // x - y*d, sign exact
   const int dir = (rho > 0.0f) - (rho < 0.0f);
   uint32_t b = __float_as_uint(y);
@@ -98,11 +103,9 @@ __device__ __forceinline__ float quot1(float x, float d, float rh, float rl) {
 }
 
 // Level-1 quotient: x / d from the two-float reciprocal, one rounding, no
-// correction (the low part is dropped when it overflows, as in quot1).
+// correction.
 __device__ __forceinline__ float quot_tf(float x, float rh, float rl) {
-  float lo = x * rl;
-  lo = __builtin_isfinite(lo) ? lo : 0.0f;
-  return __builtin_fmaf(x, rh, lo);
+  return __builtin_fmaf(x, rh, quot_low(x, rl));
 }
 
 // Fast quotient of one level: 0 = x * r (r = rh), 1 = quot_tf, 2 = quot1.
