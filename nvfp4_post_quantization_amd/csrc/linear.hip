@@ -31,6 +31,7 @@ constexpr size_t kGemmWorkspace = 32u << 20;       // hipBLASLt workspace, carve
 constexpr size_t kAlign = 256;
 constexpr int kTuneAlgos = 16;                       // heuristic candidates timed at the first call of a shape
 constexpr int kTuneReps = 2;                         // timed runs per candidate (after one warm run)
+constexpr int kTuneFinal = 4;                        // best candidates timed again before the pick
 
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -59,9 +60,12 @@ struct Layouts {
   }
 };
 
-// Time each candidate (one warm run, then kTuneReps runs between two events)
-// and return the index of the fastest that ran; candidates that fail to run
-// are skipped.  Writes y (with correct results) along the way.
+// Time each candidate: one warm run, then kTuneReps runs, each between its
+// own pair of events, scored by its fastest run; then the kTuneFinal best
+// are timed again in interleaved rounds (a candidate that drew a disturbed
+// first measurement still competes on its best), and the index of the
+// fastest is returned.  Candidates that fail to run are skipped.  Writes y
+// (with correct results) along the way.
 int tune(hipblasLtHandle_t handle, const Layouts& L, const hipblasLtMatmulHeuristicResult_t* heur, int n,
          const void* w, const void* xh, void* y, void* ws, hipStream_t s, int* pick) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -73,30 +77,56 @@ int tune(hipblasLtHandle_t handle, const Layouts& L, const hipblasLtMatmulHeuris
     return NVFP4_ERR_HIP;
   }
   const float alpha = 1.0f, beta = 0.0f;
-  float best = 0.0f;
-  int found = -1;
+  float score[kTuneAlgos];
+  bool usable[kTuneAlgos];
   int st = NVFP4_OK;
-  for (int i = 0; i < n && st == NVFP4_OK; ++i) {
-    if (heur[i].state != HIPBLAS_STATUS_SUCCESS || heur[i].workspaceSize > kGemmWorkspace) continue;
-    auto run = [&]() {
-      return hipblasLtMatmul(handle, L.desc, &alpha, w, L.a, xh, L.b, &beta, y, L.c, y, L.c, &heur[i].algo, ws,
-                             kGemmWorkspace, s);
-    };
-    if (run() != HIPBLAS_STATUS_SUCCESS) continue;
-    bool ok = hipEventRecord(e0, s) == hipSuccess;
-    for (int r = 0; r < kTuneReps && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
+  auto run = [&](int i) {
+    return hipblasLtMatmul(handle, L.desc, &alpha, w, L.a, xh, L.b, &beta, y, L.c, y, L.c, &heur[i].algo, ws,
+                           kGemmWorkspace, s) == HIPBLAS_STATUS_SUCCESS;
+  };
+  // one timed run of candidate i; false if it did not run (st set on a HIP error)
+  auto time_one = [&](int i) {
+    bool ok = hipEventRecord(e0, s) == hipSuccess && run(i);
     he = hipEventRecord(e1, s);
     if (he == hipSuccess) he = hipEventSynchronize(e1);
-    if (he != hipSuccess) { set_hip_error(he, "tuning the GEMM"); st = NVFP4_ERR_HIP; break; }
-    float ms = 0.0f;
-    if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (found < 0 || ms < best)) {
-      best = ms;
-      found = i;
+    if (he != hipSuccess) {
+      set_hip_error(he, "tuning the GEMM");
+      st = NVFP4_ERR_HIP;
+      return false;
     }
+    float ms = 0.0f;
+    ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+    if (ok && ms < score[i]) score[i] = ms;
+    return ok;
+  };
+  for (int i = 0; i < n; ++i) {
+    score[i] = __builtin_inff();
+    usable[i] = heur[i].state == HIPBLAS_STATUS_SUCCESS && heur[i].workspaceSize <= kGemmWorkspace;
   }
+  for (int i = 0; i < n && st == NVFP4_OK; ++i) {
+    if (!usable[i] || !run(i)) { usable[i] = false; continue; }
+    for (int r = 0; r < kTuneReps && usable[i] && st == NVFP4_OK; ++r) usable[i] = time_one(i);
+  }
+  // the kTuneFinal best so far, timed again round-robin
+  int top[kTuneFinal];
+  int ntop = 0;
+  for (int k = 0; k < kTuneFinal; ++k) {
+    int b = -1;
+    for (int i = 0; i < n; ++i) {
+      bool taken = false;
+      for (int j = 0; j < ntop; ++j) taken = taken || top[j] == i;
+      if (usable[i] && !taken && score[i] < __builtin_inff() && (b < 0 || score[i] < score[b])) b = i;
+    }
+    if (b >= 0) top[ntop++] = b;
+  }
+  for (int r = 0; r < kTuneReps && st == NVFP4_OK; ++r)
+    for (int j = 0; j < ntop && st == NVFP4_OK; ++j) (void)time_one(top[j]);
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (st) return st;
+  int found = -1;
+  for (int i = 0; i < n; ++i)
+    if (usable[i] && score[i] < __builtin_inff() && (found < 0 || score[i] < score[found])) found = i;
   *pick = found < 0 ? 0 : found;
   return NVFP4_OK;
 }
