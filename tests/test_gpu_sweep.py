@@ -115,10 +115,11 @@ def _scaled_correlation(c, rng, groups):
 
 @pytest.mark.parametrize("kind,rho", [("equi", 0.05), ("equi", 0.059), ("equi", 0.07), ("equi", 0.5),
                                       ("signed", 0.85), ("signed", 0.95)])
-def test_sweep_correlated_hessians(kind, rho):
+def test_sweep_correlated_hessians(kind, rho, path):
     """Row sums of |C_ij| (j != i) of 15 rho ("equi") or exactly rho with random
     signs ("signed"), below and above 0.9: the sweep's diagonal screen is on
-    for the first and off for the others; every case meets the oracle bar."""
+    for the first and off for the others; every case meets the oracle bar on
+    every E2M1 decision path (each mode has its own step loop)."""
     note(f"sweep correlated H {kind} {rho}")
     rng = np.random.default_rng(int(rho * 1000) + (7 if kind == "signed" else 0))
     groups = 8
