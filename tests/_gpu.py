@@ -52,18 +52,21 @@ def rel_frobenius(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.where(den > 0, num / np.maximum(den, 1e-300), num)
 
 
-def compare_sweep(w_bits, h32, s2, packed, codes, cost, max_mismatch_frac=1e-4):
+def compare_sweep(w_bits, h32, s2, packed, codes, cost, max_mismatch_frac=1e-4, costs=None):
     """Sweep parity of GPU outputs (packed, codes, cost) for the rows w_bits.
 
     Per block: the code equals the oracle's argmin on >= 1 - max_mismatch_frac
     of the blocks; where it differs, the oracle's cost of the GPU code is within
     1e-5 relative of the oracle minimum; the nibbles always equal the oracle's
     quantization at the GPU code, bit for bit; the fp32 cost is within 1e-4
-    relative of the oracle's cost of that code.  Returns the mismatch count."""
+    relative of the oracle's cost of that code.  costs, when given, are the
+    oracle's sweep_costs of the same rows (computed elsewhere, e.g. in a
+    process pool).  Returns the mismatch count."""
     from oracle import nvfp4 as N
     from oracle import formats as F
     h = np.asarray(h32, dtype=np.float32).astype(np.float64)
-    costs = N.sweep_costs(w_bits, h, s2)                        # [rows, G, 127]
+    if costs is None:
+        costs = N.sweep_costs(w_bits, h, s2)                    # [rows, G, 127]
     ref = np.argmin(costs, axis=2)
     ref_min = np.min(costs, axis=2)
     rows, g = codes.shape
