@@ -16,8 +16,10 @@
  *   library keeps no pointer after a call returns and allocates no device
  *   memory of its own, except the hipBLASLt handle that
  *   nvfp4_quantlinear_forward creates on its first call on a device (kept
- *   until the process ends); scratch memory comes in as a caller-provided
- *   workspace.
+ *   until the process ends) and the static 8 MiB buffer of
+ *   nvfp4_hessian_accum_noalloc (part of the library's device code, present
+ *   on each device once the library runs there); scratch memory otherwise
+ *   comes in as a caller-provided workspace.
  * - bf16 values are passed as uint16_t bit patterns.  Matrices are row-major;
  *   "ld" arguments are row strides in ELEMENTS.  Blocks of 16 run along the
  *   last (contiguous) axis.
@@ -61,7 +63,9 @@ enum nvfp4_status {
                                  function requires (16 bytes for bf16 rows)       */
   NVFP4_ERR_WORKSPACE = 4,    /* workspace smaller than the matching *_bytes() query */
   NVFP4_ERR_BAD_INPUT = 5,    /* an argument value is out of range (e.g. mats <= 0)  */
-  NVFP4_ERR_HIP = 6           /* a HIP launch or API call failed                     */
+  NVFP4_ERR_HIP = 6,          /* a HIP launch or API call failed                     */
+  NVFP4_ERR_SCRATCH_LIMIT = 7 /* the input needs more scratch than the static buffer
+                                 of nvfp4_hessian_accum_noalloc holds               */
 };
 
 /* Text for a status code (static storage; for NVFP4_ERR_HIP the text of the
@@ -114,6 +118,28 @@ size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k);
 int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
                         float* H, float* amax_inout, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_hessian_accum without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same operation, kernels and results (bit for bit)
+ * as nvfp4_hessian_accum; the fp32 partial slots live in a static device
+ * buffer of 8 MiB inside the library instead (each GPU the library runs on
+ * holds its own copy until the process ends), which fits every shape with
+ * k <= 65536 and any token count.  The call allocates nothing; its first
+ * call on a device looks up that device's buffer address
+ * (hipGetSymbolAddress) with the device current.  All calls on one GPU share
+ * the buffer: calls that overlap in time on one GPU (two host threads, or
+ * two streams whose work may run concurrently) race and give wrong H; order
+ * them on one stream or with events.  Nothing in the buffer needs clearing
+ * between calls.
+ * x, tokens, k, ldx, H, amax_inout, stream: as for nvfp4_hessian_accum.
+ * Errors: as for nvfp4_hessian_accum without WORKSPACE, plus SCRATCH_LIMIT
+ *         when nvfp4_hessian_workspace_bytes' plain-kernel share exceeds the
+ *         8 MiB buffer (k > 65536), and HIP (also a failed address lookup).
+ */
+int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
+                                float* H, float* amax_inout, void* stream);
 
 /*
  * Step 2 for a W4A4 calibration, where the Linear's input passes through its

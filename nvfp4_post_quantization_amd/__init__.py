@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
-    "hessian_accum", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
+    "hessian_accum", "hessian_accum_noalloc", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
     "fp8_compute_scale", "fp8_quantize", "fp8_dequant", "block_hadamard", "hessian_hadamard",
     "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward",
 ]
@@ -37,6 +37,7 @@ _SIGS = {
     "nvfp4_hessian_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_hessian_accum": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                            ctypes.c_size_t, _c_void_p]),
+    "nvfp4_hessian_accum_noalloc": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "nvfp4_hessian_accum_fq": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                               _c_void_p, ctypes.c_size_t, _c_void_p]),
     "nvfp4_scale_sweep": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
@@ -159,6 +160,23 @@ def hessian_accum(x: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = 
     _check("nvfp4_hessian_accum", load().nvfp4_hessian_accum(
         x.data_ptr(), tokens, k, ldx, H.data_ptr(), amax.data_ptr() if amax is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return H
+
+
+def hessian_accum_noalloc(x: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = None) -> torch.Tensor:
+    """hessian_accum without a workspace: the library's static per-device
+    buffer holds the partial slots (k <= 65536).  Calls that overlap in time
+    on one GPU race on that buffer."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(H, torch.float32, "H")
+    tokens, k = x.shape
+    if H.numel() != (k // 16) * 256 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [k/16, 16, 16] tensor")
+    ldx = _row_major(x, "x")
+    if amax is not None:
+        _dev(amax, torch.float32, "amax")
+    _check("nvfp4_hessian_accum_noalloc", load().nvfp4_hessian_accum_noalloc(
+        x.data_ptr(), tokens, k, ldx, H.data_ptr(), amax.data_ptr() if amax is not None else None, _stream(x)))
     return H
 
 

@@ -59,6 +59,8 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_WORKSPACE: return "workspace smaller than the size the matching *_bytes query returns";
     case NVFP4_ERR_BAD_INPUT: return "argument value out of range";
     case NVFP4_ERR_HIP: return g_hip_error;
+    case NVFP4_ERR_SCRATCH_LIMIT:
+      return "input needs more scratch than the static buffer of the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -96,6 +98,19 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
   int st = check_hessian(x, tokens, k, ldx, H, workspace, workspace_bytes);
   if (st || tokens == 0) return st;
   return launch_hessian_accum(x, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
+}
+
+int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H,
+                                float* amax_inout, void* stream) {
+  int st = check_matrix(tokens, k, ldx, 2);
+  if (st) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL_ARG;
+  if (tokens == 0) return NVFP4_OK;
+  if ((st = check_bf16_rows(x, ldx))) return st;
+  if (!aligned16(H)) return NVFP4_ERR_MISALIGNED;
+  if (hessian_plain_workspace_bytes(tokens, k) > kHessianScratchBytes) return NVFP4_ERR_SCRATCH_LIMIT;
+  return launch_hessian_accum_noalloc(x, tokens, k, ldx, H, amax_inout, as_stream(stream));
 }
 
 int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,

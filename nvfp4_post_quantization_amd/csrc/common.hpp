@@ -37,6 +37,12 @@ int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t 
 int launch_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2, int64_t rows, int64_t k,
                    uint16_t* out, hipStream_t s);
 size_t hessian_workspace_bytes(int64_t tokens, int64_t k);
+// partial slots of the plain accumulate alone, and the static buffer that
+// holds them for nvfp4_hessian_accum_noalloc
+size_t hessian_plain_workspace_bytes(int64_t tokens, int64_t k);
+constexpr size_t kHessianScratchBytes = size_t(8) << 20;
+int launch_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
+                                 hipStream_t s);
 int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
                          void* workspace, hipStream_t s);
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,

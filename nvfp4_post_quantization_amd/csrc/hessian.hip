@@ -24,8 +24,17 @@
 // The W4A4 variant (nvfp4_hessian_accum_fq) accumulates the Hessian of the
 // fake-quantized input instead: each lane pair quantizes its 16-element
 // block in registers before the tile goes to LDS.
+#include <mutex>
+
 #include "common.hpp"
 #include "nvfp4_device.hpp"
+
+// Partial slots of nvfp4_hessian_accum_noalloc: the plain kernel's workspace
+// for any shape with k <= 65536 (512 workgroups x 2 slabs x 8 groups x 1 KiB),
+// held by each device that runs the library until the process ends.  Host
+// code never passes this name to a kernel: it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[nvfp4::kHessianScratchBytes];
 
 namespace nvfp4 {
 
@@ -436,6 +445,43 @@ int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t l
                                                                p.slabs, p.streams, ws, amax);
   int st = launch_status("hessian_partial_kernel");
   return st ? st : launch_reduce(p, k, ws, H, s);
+}
+
+size_t hessian_plain_workspace_bytes(int64_t tokens, int64_t k) {
+  return plan_bytes(plan(tokens, k, kTargetWgs));
+}
+
+// Device address of `scratch` per device, looked up once per device with
+// that device current (each device holds its own copy of the array).
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {};
+
+static int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return NVFP4_ERR_BAD_INPUT;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return hip_status(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
+// The plain accumulate with its partial slots in `scratch` (the caller has
+// checked that the plan fits).  Every slot the reduce reads is written by
+// the partial kernel of the same call, so nothing needs clearing.
+int launch_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
+                                 hipStream_t s) {
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st) return st;
+  return launch_hessian_accum(x, tokens, k, ldx, H, amax, ws, s);
 }
 
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,

@@ -15,7 +15,7 @@ import nvfp4_post_quantization_amd as nq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4mi.h")
 
-OK, NULL, SHAPE, ALIGN, WS, BADIN, HIP = 0, 1, 2, 3, 4, 5, 6
+OK, NULL, SHAPE, ALIGN, WS, BADIN, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 P = 0x10000          # a 16-byte-aligned fake address (never dereferenced)
 
 
@@ -36,7 +36,7 @@ def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) == {
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
-        "nvfp4_hessian_accum", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
+        "nvfp4_hessian_accum", "nvfp4_hessian_accum_noalloc", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
         "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant", "nvfp4_scale_sweep_ex",
         "nvfp4_quantlinear_workspace_bytes", "nvfp4_quantlinear_forward",
@@ -49,8 +49,9 @@ def test_header_symbols_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 7):
+    for s in range(0, 8):
         assert lib.nvfp4_status_string(s)
+    assert b"static buffer" in lib.nvfp4_status_string(SCRATCH)
     assert lib.nvfp4_status_string(0) == b"ok"
     assert b"unknown" in lib.nvfp4_status_string(99)
 
@@ -83,6 +84,24 @@ def test_hessian_validation(lib):
     assert f(P, 16, 32, 32, P, None, None, need, None) == NULL
     assert f(P, 0, 32, 32, P, None, None, 0, None) == OK                  # nothing to do
     assert f(P, 1 << 62, 32, 1 << 40, P, None, P, 1 << 20, None) == SHAPE   # overflow
+
+
+def test_hessian_noalloc_validation(lib):
+    f = lib.nvfp4_hessian_accum_noalloc
+    assert f(P, 16, 24, 24, P, None, None) == SHAPE                       # k % 16
+    assert f(P, 16, 32, 16, P, None, None) == SHAPE                       # ld < k
+    assert f(P, -1, 32, 32, P, None, None) == SHAPE
+    assert f(P, 16, 32, 32, None, None, None) == NULL
+    assert f(None, 16, 32, 32, P, None, None) == NULL
+    assert f(P + 2, 16, 32, 32, P, None, None) == ALIGN
+    assert f(P, 16, 32, 36, P, None, None) == ALIGN                       # row stride not 16 B
+    assert f(P, 16, 32, 32, P + 4, None, None) == ALIGN                   # H
+    assert f(P, 0, 32, 32, P, None, None) == OK                           # nothing to do
+    assert f(P, 1 << 62, 32, 1 << 40, P, None, None) == SHAPE             # overflow
+    # beyond the static buffer: 513 slabs of 8 groups need three partial
+    # slots per workgroup (12 MiB); rejected before any HIP call
+    assert f(P, 65536, 65552, 65552, P, None, None) == SCRATCH
+    assert f(P, 64, 65552, 65552, P, None, None) == SCRATCH
 
 
 def test_hessian_fq_validation(lib):
