@@ -38,6 +38,13 @@
  *   place by design).  Calls are reentrant; concurrent calls must not share
  *   outputs or workspaces.
  * - Inputs are expected to be finite.  NaN/Inf inputs give unspecified codes.
+ * - Test hook: the environment variable NVFP4MI_FORCE_EXACT, read at every
+ *   launch of the quantizers, the sweep, the W4A4 Hessian and the fake QDQ,
+ *   selects which of the certified E2M1 decision paths may be used (unset or
+ *   0: all; 1: exact thresholds only; 2: not the one-float reciprocal; 3:
+ *   neither of the uncorrected reciprocals).  Every path gives the same
+ *   bits, so it changes speed, not results; the tests use it to run every
+ *   case on each path.
  *
  * Rounding (readings of the pages, which name no rounding mode): every
  * encode rounds the exact real quotient once to nearest, ties to even, and

@@ -24,7 +24,7 @@ __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
     "hessian_accum", "hessian_accum_noalloc", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
     "fp8_compute_scale", "fp8_quantize", "fp8_dequant", "block_hadamard", "hessian_hadamard",
-    "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward",
+    "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward", "scale_sweep_stats",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
@@ -55,6 +55,11 @@ _SIGS = {
     "nvfp4_block_hadamard": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p]),
     "nvfp4_hessian_hadamard": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p]),
     "nvfp4_fakequant": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i64, _c_void_p]),
+    "nvfp4_scale_sweep_stats": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                               _c_void_p, _c_void_p, _c_void_p]),
+    "nvfp4_probe_read": (ctypes.c_int, [_c_void_p, ctypes.c_size_t, _c_void_p, ctypes.c_int, _c_void_p]),
+    "nvfp4_probe_write": (ctypes.c_int, [_c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int, _c_void_p]),
+    "nvfp4_probe_copy": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_size_t, ctypes.c_int, _c_void_p]),
     "nvfp4_quantlinear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_quantlinear_forward": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64,
                                                  _c_void_p, _i64, _c_void_p, ctypes.c_size_t, _c_void_p]),
@@ -395,3 +400,30 @@ def quantlinear_forward(x: torch.Tensor, x_scale2: torch.Tensor, w_hat: torch.Te
         x.data_ptr(), tokens, k, ldx, x_scale2.data_ptr(), w_hat.data_ptr(), o, ldw, out.data_ptr(), ldy,
         workspace.data_ptr(), workspace.numel(), _stream(x)))
     return out
+
+
+def scale_sweep_stats(w: torch.Tensor, H: torch.Tensor, scale2: torch.Tensor, stats: torch.Tensor | None = None,
+                      out=None):
+    """The sweep's counting build (measurement): scale_sweep's outputs bit for
+    bit, plus its search counters added to stats (int64[6] on the device:
+    evaluated codes, wave steps, full-form steps, screen steps, blocks,
+    waves).  Returns (packed, codes, stats)."""
+    _dev(w, torch.bfloat16, "w", 2)
+    _dev(H, torch.float32, "H")
+    _dev(scale2, torch.float32, "scale2")
+    rows, k = w.shape
+    if H.numel() != (k // 16) * 256 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [k/16, 16, 16] tensor")
+    ldw = _row_major(w, "w")
+    if stats is None:
+        stats = torch.zeros(6, dtype=torch.int64, device=w.device)
+    _dev(stats, torch.int64, "stats")
+    if out is None:
+        packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=w.device)
+        codes = torch.empty((rows, k // 16), dtype=torch.uint8, device=w.device)
+    else:
+        packed, codes = out
+    _check("nvfp4_scale_sweep_stats", load().nvfp4_scale_sweep_stats(
+        w.data_ptr(), rows, k, ldw, H.data_ptr(), scale2.data_ptr(), packed.data_ptr(), codes.data_ptr(),
+        stats.data_ptr(), _stream(w)))
+    return packed, codes, stats

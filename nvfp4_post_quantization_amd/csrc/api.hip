@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "common.hpp"
+#include "../../include/nvfp4mi_probe.h"
 
 namespace nvfp4 {
 
@@ -123,7 +124,8 @@ int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t
 }
 
 static int scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
-                       uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu, void* stream) {
+                       uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu, void* stream,
+                       uint64_t* stats = nullptr) {
   int st = check_matrix(rows, k, ldw, 2);
   if (st) return st;
   if (k % 16) return NVFP4_ERR_BAD_SHAPE;
@@ -131,6 +133,8 @@ static int scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, 
   if (!H || !scale2 || ((!w || !packed || !codes) && rows > 0)) return NVFP4_ERR_NULL_ARG;
   if (rows == 0) return NVFP4_OK;
   if ((st = check_bf16_rows(w, ldw))) return st;
+  if (!aligned8(packed) || !aligned4(cost) || !aligned8(stats)) return NVFP4_ERR_MISALIGNED;
+  if (stats) return launch_scale_sweep_stats(w, rows, k, ldw, H, scale2, packed, codes, stats, as_stream(stream));
   return launch_scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, wgs_per_cu, as_stream(stream));
 }
 
@@ -142,6 +146,42 @@ int nvfp4_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, c
 int nvfp4_scale_sweep_ex(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H, const float* scale2,
                          uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu, void* stream) {
   return scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, cost, wgs_per_cu, stream);
+}
+
+int nvfp4_scale_sweep_stats(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
+                            const float* scale2, uint8_t* packed, uint8_t* codes, uint64_t* stats, void* stream) {
+  if (!stats) return NVFP4_ERR_NULL_ARG;
+  return scale_sweep(w, rows, k, ldw, H, scale2, packed, codes, nullptr, 0, stream, stats);
+}
+
+static int check_probe(const void* p, size_t bytes, int wgs) {
+  if (bytes % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (wgs < 0 || wgs > 65535) return NVFP4_ERR_BAD_INPUT;
+  if (!p) return NVFP4_ERR_NULL_ARG;
+  if (!aligned16(p)) return NVFP4_ERR_MISALIGNED;
+  return NVFP4_OK;
+}
+
+int nvfp4_probe_read(const void* buf, size_t bytes, void* sink, int workgroups, void* stream) {
+  int st = check_probe(buf, bytes, workgroups);
+  if (st) return st;
+  if (!sink) return NVFP4_ERR_NULL_ARG;
+  if (!aligned4(sink)) return NVFP4_ERR_MISALIGNED;
+  return bytes ? launch_probe_read(buf, bytes, sink, workgroups, as_stream(stream)) : NVFP4_OK;
+}
+
+int nvfp4_probe_write(void* buf, size_t bytes, uint32_t value, int workgroups, void* stream) {
+  const int st = check_probe(buf, bytes, workgroups);
+  if (st) return st;
+  return bytes ? launch_probe_write(buf, bytes, value, workgroups, as_stream(stream)) : NVFP4_OK;
+}
+
+int nvfp4_probe_copy(const void* src, void* dst, size_t bytes, int workgroups, void* stream) {
+  int st = check_probe(src, bytes, workgroups);
+  if (st || (st = check_probe(dst, bytes, workgroups))) return st;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return NVFP4_ERR_BAD_INPUT;       // overlap
+  return bytes ? launch_probe_copy(src, dst, bytes, workgroups, as_stream(stream)) : NVFP4_OK;
 }
 
 int nvfp4_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,

@@ -22,6 +22,8 @@ inline int launch_status(const char* where) { return hip_status(hipGetLastError(
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Test hook read from the environment: NVFP4MI_FORCE_EXACT=1 disables the
 // certified FP4-convert fast paths (exact thresholds everywhere); =2 skips the
@@ -65,6 +67,14 @@ void set_error_text(const char* fmt, ...);
 int launch_scale_sweep(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
                        const float* scale2, uint8_t* packed, uint8_t* codes, float* cost, int wgs_per_cu,
                        hipStream_t s);
+// the counting build (nvfp4_scale_sweep_stats), uncapped
+int launch_scale_sweep_stats(const uint16_t* w, int64_t rows, int64_t k, int64_t ldw, const float* H,
+                             const float* scale2, uint8_t* packed, uint8_t* codes, uint64_t* stats,
+                             hipStream_t s);
+// measurement support (include/nvfp4mi_probe.h)
+int launch_probe_read(const void* buf, size_t bytes, void* sink, int wgs, hipStream_t s);
+int launch_probe_write(void* buf, size_t bytes, uint32_t value, int wgs, hipStream_t s);
+int launch_probe_copy(const void* src, void* dst, size_t bytes, int wgs, hipStream_t s);
 int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,
                    uint8_t* codes, float* scale2, int64_t* fallback, hipStream_t s);
 

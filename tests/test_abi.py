@@ -13,16 +13,19 @@ import pytest
 import nvfp4_post_quantization_amd as nq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "nvfp4mi.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("nvfp4mi.h", "nvfp4mi_probe.h")]
 
 OK, NULL, SHAPE, ALIGN, WS, BADIN, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 P = 0x10000          # a 16-byte-aligned fake address (never dereferenced)
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z0-9_]+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z0-9_]+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +43,9 @@ def test_header_symbols_exported(lib):
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
         "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant", "nvfp4_scale_sweep_ex",
         "nvfp4_quantlinear_workspace_bytes", "nvfp4_quantlinear_forward",
+        "nvfp4_probe_read", "nvfp4_probe_write", "nvfp4_probe_copy", "nvfp4_scale_sweep_stats",
     }
+    assert {os.path.basename(h) for h in HEADERS} == set(os.listdir(os.path.join(ROOT, "include")))
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(nq.LIB_PATH)
@@ -127,6 +132,8 @@ def test_sweep_quant_dequant_validation(lib):
     assert s(P, 4, 32, 32, P, None, P, P, None, None) == NULL
     assert s(P, 4, 32, 32, P, P, None, P, None, None) == NULL
     assert s(P + 8, 4, 32, 32, P, P, P, P, None, None) == ALIGN
+    assert s(P, 4, 32, 32, P, P, P + 4, P, None, None) == ALIGN          # packed: 8-byte stores
+    assert s(P, 4, 32, 32, P, P, P, P, P + 2, None) == ALIGN             # cost: float stores
     assert s(P, 0, 32, 32, P, P, P, P, None, None) == OK
     qd = lib.nvfp4_quantize_dynamic
     assert qd(P, 4, 40, 40, P, P, P, None) == SHAPE
@@ -235,3 +242,32 @@ def test_sweep_ex_validation(lib):
     assert s(P, 4, 24, 24, P, P, P, P, None, 1, None) == SHAPE
     assert s(P, 4, 32, 32, None, P, P, P, None, 1, None) == NULL
     assert s(P, 0, 32, 32, P, P, None, None, None, 1, None) == OK
+
+
+def test_probe_and_stats_validation(lib):
+    r, w, c = lib.nvfp4_probe_read, lib.nvfp4_probe_write, lib.nvfp4_probe_copy
+    assert r(P, 24, P, 0, None) == SHAPE                     # bytes % 16
+    assert r(None, 32, P, 0, None) == NULL
+    assert r(P, 32, None, 0, None) == NULL                   # sink
+    assert r(P + 8, 32, P, 0, None) == ALIGN
+    assert r(P, 32, P + 2, 0, None) == ALIGN
+    assert r(P, 32, P, -1, None) == BADIN                    # workgroups
+    assert r(P, 32, P, 65536, None) == BADIN
+    assert r(P, 0, P, 0, None) == OK
+    assert w(P, 20, 0, 0, None) == SHAPE
+    assert w(None, 32, 0, 0, None) == NULL
+    assert w(P + 4, 32, 0, 0, None) == ALIGN
+    assert w(P, 32, 0, -2, None) == BADIN
+    assert w(P, 0, 0, 0, None) == OK
+    assert c(P, P + 4096, 24, 0, None) == SHAPE
+    assert c(None, P, 32, 0, None) == NULL
+    assert c(P, None, 32, 0, None) == NULL
+    assert c(P, P + 8, 32, 0, None) == ALIGN
+    assert c(P, P + 16, 32, 0, None) == BADIN                # overlapping
+    assert c(P, P + 4096, 32, 70000, None) == BADIN
+    assert c(P, P + 4096, 0, 0, None) == OK
+    st = lib.nvfp4_scale_sweep_stats
+    assert st(P, 4, 32, 32, P, P, P, P, None, None) == NULL           # stats
+    assert st(P, 4, 24, 24, P, P, P, P, P, None) == SHAPE
+    assert st(P, 4, 32, 32, P, P, P, P, P + 4, None) == ALIGN          # stats: uint64
+    assert st(P, 0, 32, 32, P, P, P, P, P, None) == OK
