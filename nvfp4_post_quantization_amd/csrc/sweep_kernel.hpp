@@ -56,7 +56,13 @@
 //    bit for bit;
 //  * the wave steps until all its lanes are done (lanes that finish early
 //    idle); the nibbles are re-quantized at the chosen code.
-//  * two workgroups per CU (launch bounds): 249 VGPRs, no scratch.  The
+//  * weights are read with non-temporal loads, workgroups are ordered so
+//    that 32 x-neighbours share an XCD, and outputs go through LDS: the last
+//    of a workgroup's waves to finish writes all its rows, four groups (32
+//    bytes of nibbles, 4 code bytes) per row at a time.  The sweep runs
+//    beside the HBM-bound Hessian accumulate, which its row-scattered reads
+//    and writes had slowed by about 8%;
+//  * two workgroups per CU (launch bounds): 256 VGPRs, no scratch.  The
 //    occupancy-capped launch (one workgroup per CU, for running beside
 //    another kernel) reserves dynamic LDS so that a second one cannot fit.
 // fp32 MFMA and fp32 VALU share one datapath on this chip (measured: their
@@ -80,6 +86,10 @@ constexpr float kPruneMargin = 2e-5f;
 // sweep from 0.905 to 0.81 ms and the gate sweep from 0.873 to 0.838 ms, half
 // the per-workgroup set-up; 1024 leaves too little to balance when capped).
 constexpr int64_t kSweepWgs = 2048;
+// Rows of a workgroup's outputs that can be staged in LDS (8 batches of 64);
+// the launcher keeps rows_per_wg within it for any row count below 2^25.
+constexpr int kStageRows = 512;
+constexpr int kStageBatches = kStageRows / 64;
 
 // Value of v in lane src (a constant), broadcast through scalar registers.
 __device__ __forceinline__ double bcast(double v, int src) {
@@ -205,6 +215,32 @@ __device__ float screen_factor(const float* Hg, int lane) {
 // step's quantization and quadratic form.  MODE 2 (per-code levels) reads
 // the tables at each step.  Every lane computes exactly what the table reads
 // would give.
+// XCD-aware workgroup order.  The dispatcher places workgroup L (linear id)
+// on XCD L % 8, and each XCD has its own L2.  Runs of kXcdBand workgroups
+// that are neighbours in x (the same rows, consecutive groups: 32 x 4 groups
+// = 1 KiB of each row's packed output and 128 bytes of its codes, whole
+// lines) are placed on one XCD instead of spread over all eight, so that
+// their reads of a row's weights and their writes of its outputs meet in one
+// L2.  Measured beside the Hessian accumulate: 0.2-0.25 ms less per
+// benchmark step.  A permutation of the grid; the last (total mod 8
+// kXcdBand) workgroups keep their place.
+constexpr uint32_t kXcds = 8;
+constexpr uint32_t kXcdBand = 32;
+
+__device__ __forceinline__ void sweep_wg_coords(int64_t* bx, int64_t* by) {
+  const uint32_t gx = gridDim.x, total = gx * gridDim.y;
+  const uint32_t L = blockIdx.x + blockIdx.y * gx;
+  const uint32_t full = total / (kXcdBand * kXcds) * (kXcdBand * kXcds);
+  uint32_t lam = L;
+  if (L < full) {
+    const uint32_t c = L % kXcds, s = L / kXcds;
+    const uint32_t xi = s % kXcdBand, q = kXcds * (s / kXcdBand) + c;
+    lam = q * kXcdBand + xi;
+  }
+  *bx = lam % gx;
+  *by = lam / gx;
+}
+
 // Work counters of the counting build (wave-uniform, in scalar registers).
 struct SweepStats {
   uint32_t evals, steps, forms, screens;
@@ -317,7 +353,16 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
   __shared__ int32_t tp[128];
   __shared__ float sqS[kWaves][16];
   __shared__ __attribute__((aligned(16))) float Hs[kWaves][256];
+  // Output staging: each wave puts its batches' nibbles and codes here, and
+  // the last of the workgroup's waves to finish writes them all out, a row's
+  // four groups together (one 32-byte nibble segment and one 4-byte code word
+  // per row instead of four 8-byte and four 1-byte stores at different
+  // times).
+  __shared__ __attribute__((aligned(16))) uint2 st_nib[kStageRows][kWaves];
+  __shared__ uint32_t st_code[kStageRows];
+  __shared__ uint32_t st_done[kStageBatches];
   const float s2 = *scale2;
+  if (threadIdx.x < kStageBatches) st_done[threadIdx.x] = 0u;
   build_code_search(tp, s2);
   build_code_tables(t, s2, force_exact);                     // syncs
   const int mode = table_mode(t);
@@ -325,7 +370,10 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
   const int64_t groups = k >> 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
+  int64_t bx, by;
+  sweep_wg_coords(&bx, &by);
+  const int64_t g0 = bx * kWaves;                            // the workgroup's first group
+  const int64_t g = g0 + wave;
   if (g < groups) {
     schur_sqrt(H + g * 256, lane, sqS[wave]);
 #pragma unroll
@@ -344,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
   const float thr_scale = 1.0f + kPruneMargin;
   const float mu2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(screen_factor(Hg, lane))));
 
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
+  const int64_t r0 = by * rows_per_wg;
   int64_t r1 = r0 + rows_per_wg;
   if (r1 > rows) r1 = rows;
   SweepStats st{0u, 0u, 0u, 0u};
@@ -357,7 +405,9 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
     {
       const int64_t rr = valid ? r : rb;                     // rb < r1 always holds
       const uint4* src = reinterpret_cast<const uint4*>(w + rr * ldw + g * 16);
-      const uint4 v0 = src[0], v1 = src[1];
+      // non-temporal: a weight is read once (measured beside the Hessian
+      // accumulate: 0.15 ms less per benchmark step than cached loads)
+      const uint4 v0 = ld_nt4(src), v1 = ld_nt4(src + 1);
       const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) { wv[2 * i] = bf16lo(u[i]); wv[2 * i + 1] = bf16hi(u[i]); }
@@ -395,11 +445,59 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
     } else {
       search_block<2, STATS>(wv, a, b, c0, done, best, bestc, t, Hg, hh, thr_scale, mu2, st);
     }
-    if (valid) {
-      const uint2 nb = nibbles16(wv, bestc, t, mode);
-      *reinterpret_cast<uint2*>(packed + r * (k >> 1) + g * 8) = nb;
-      codes[r * groups + g] = (uint8_t)bestc;
-      if (!STATS && cost) cost[r * groups + g] = best;
+    const uint2 nb = nibbles16(wv, bestc, t, mode);
+    float* const cost_out = STATS ? nullptr : cost;
+    if (rows_per_wg > kStageRows) {                          // (only for huge row counts) direct stores
+      if (valid) {
+        *reinterpret_cast<uint2*>(packed + r * (k >> 1) + g * 8) = nb;
+        codes[r * groups + g] = (uint8_t)bestc;
+        if (cost_out) cost_out[r * groups + g] = best;
+      }
+      continue;
+    }
+    const int j = (int)((rb - r0) >> 6);                     // batch within the workgroup
+    const int sr = j * 64 + lane;                            // staging row
+    st_nib[sr][wave] = nb;
+    reinterpret_cast<uint8_t*>(&st_code[sr])[wave] = (uint8_t)bestc;
+    if (cost_out && valid) cost_out[r * groups + g] = best;   // optional output: not staged
+    // publish the batch; the wave that completes the count writes it out
+    // (the release orders every lane's staging stores before lane 0's add)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    uint32_t prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&st_done[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
+    // waves of this workgroup with a group (the others returned above); each
+    // wave runs the batches in order, so the last to finish the last batch
+    // is the last to finish, and it writes every batch out
+    const uint32_t nw = (uint32_t)(groups - g0 < kWaves ? groups - g0 : kWaves);
+    const int nbat = (int)((r1 - r0 + 63) >> 6);
+    if (j == nbat - 1 && prev + 1 == nw) {
+      __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      // whole-row-segment stores where the destinations allow them (uniform)
+      const bool nib16 = nw == kWaves && ((k >> 1) % 16) == 0 && (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
+      const bool code4 = nw == kWaves && (groups % 4) == 0 && (reinterpret_cast<uintptr_t>(codes) & 3) == 0;
+      for (int jb = 0; jb < nbat; ++jb) {
+        const int sw = jb * 64 + lane;                       // staging row of output row ro
+        const int64_t ro = r0 + jb * 64 + lane;
+        if (ro < r1) {
+          uint8_t* pd = packed + ro * (k >> 1) + g0 * 8;
+          if (nib16) {
+            const uint4* src = reinterpret_cast<const uint4*>(&st_nib[sw][0]);
+            reinterpret_cast<uint4*>(pd)[0] = src[0];
+            reinterpret_cast<uint4*>(pd)[1] = src[1];
+          } else {
+            for (uint32_t q = 0; q < nw; ++q) reinterpret_cast<uint2*>(pd)[q] = st_nib[sw][q];
+          }
+          uint8_t* cd = codes + ro * groups + g0;
+          const uint32_t cw = st_code[sw];
+          if (code4) {
+            *reinterpret_cast<uint32_t*>(cd) = cw;
+          } else {
+            for (uint32_t q = 0; q < nw; ++q) cd[q] = (uint8_t)(cw >> (8 * q));
+          }
+        }
+      }
     }
   }
   if constexpr (STATS) {
@@ -425,6 +523,7 @@ inline dim3 sweep_grid(int64_t rows, int64_t k, int64_t* rows_per_wg) {
   int64_t rpw = (rows * gx + kSweepWgs - 1) / kSweepWgs;
   rpw = ((rpw + 63) / 64) * 64;
   if (rpw < 64) rpw = 64;
+  if (rpw > kStageRows) rpw = kStageRows;                   // outputs staged in LDS (more workgroups instead)
   int64_t chunks = (rows + rpw - 1) / rpw;
   while (chunks > 65535) {
     rpw *= 2;
