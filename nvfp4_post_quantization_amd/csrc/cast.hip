@@ -22,8 +22,9 @@
 //  (2) one thread per group: k_max from the nx partials, scale_2 =
 //      2^(k_max - 8) (2^-8 when the group has no valid exponent), fallback
 //      count 0;
-//  (3) codes and fallbacks for every MX block (one atomic add per workgroup
-//      for the fallback count).
+//  (3) codes for every MX block, with the workgroup's fallback blocks
+//      requantized together at its end (one atomic add per workgroup for the
+//      fallback count).
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -142,32 +143,23 @@ __device__ __forceinline__ uint32_t fallback_requant(uint4 v, int delta, uint8_t
   return codes;
 }
 
-__device__ __forceinline__ uint32_t fallback_block(uint8_t* nib16, int delta) {
-  return fallback_requant(*reinterpret_cast<const uint4*>(nib16), delta, nib16);
-}
-
-// Codes for one MX block with E8M0 byte b; may rewrite its nibbles.
-__device__ __forceinline__ uint32_t mx_block_codes(uint32_t b, int32_t kmax_code, uint8_t* nib16, int& nfb) {
-  if (b == 0xFFu) return 0x7F7Fu;
-  const int delta = kmax_code - (int)b;
-  if (delta <= 17) {
-    const uint32_t c = pow2_code(8 - delta);
-    return c | (c << 8);
-  }
-  ++nfb;
-  return fallback_block(nib16, delta);
-}
-
 // Pass 3: workgroup (x, g) takes steps x, x + nx, ... of group g; a thread
 // takes 8 consecutive MX blocks (one 8-byte E8M0 load, one 16-byte code
 // store, so each wave instruction covers one contiguous run) where the step is
 // 8-aligned and whole, single blocks otherwise.  The code pair of an E8M0 byte
 // depends only on it and the group's k_max, so the workgroup first tabulates
 // all 256 bytes in LDS (kFallback marks a block outside the window); the next
-// step's exponents are loaded before the current step is coded, and the
-// fallback blocks of a step are finished one step later (measured: a separate
-// pass for the scattered fallback rewrites is far slower than this).
+// step's exponents are loaded before the current step is coded.
+// Fallback blocks are rare and scattered.  A step stores the usual fallback
+// code pair 0x0101 as a placeholder and appends the block to a list in LDS;
+// after its last step the workgroup requantizes the whole list at once, each
+// thread taking one block with every nibble load issued before the first is
+// used (measured: per-lane handling inside the steps, even deferred by one
+// step, cost about 50 us of the pass on the MoE expert set).  Only a block
+// with an all-zero half needs its codes patched.  Blocks beyond the list's
+// capacity (not seen with realistic exponents) are handled at once.
 constexpr uint32_t kFallback = 0xFFFFu;
+constexpr int kFbCap = 2048;                            // fallback blocks listed per workgroup
 
 __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restrict__ packed,
                                                               const uint8_t* __restrict__ e8m0,
@@ -175,6 +167,10 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
                                                               uint8_t* __restrict__ codes,
                                                               unsigned long long* fallback) {
   __shared__ uint32_t tab[256];
+  __shared__ uint32_t fb_j[kFbCap];                     // block index within the group
+  __shared__ uint8_t fb_d[kFbCap];                      // its delta = k_max - k_j
+  __shared__ uint32_t fb_n;
+  __shared__ int part[kThreads / 64];
   const int64_t g = blockIdx.y;
   const int64_t nx = gridDim.x;
   // scale_2 = 2^(km - 135): km from its exponent field, or from the position
@@ -189,31 +185,24 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
     else t = kFallback;
     tab[b] = t;
   }
+  if (threadIdx.x == 0) fb_n = 0u;
   __syncthreads();
   const int64_t base = g * per_group;
   const bool aligned = ((reinterpret_cast<uintptr_t>(e8m0 + base) & 7u) == 0);
   const int64_t step = nx * kCodesChunk;
   int nfb = 0;
-  // Fallback blocks are rare and scattered; their nibble loads are issued in
-  // one step and finished in the next, so the wave does not wait on them.
-  // Up to kDefer per lane and step are deferred (the rest, almost never
-  // needed, are done at once).  The step stores the usual fallback code pair
-  // 0x0101 as a placeholder; only a block with an all-zero half needs a patch.
-  constexpr int kDefer = 2;
-  uint4 pend_v[kDefer];
-  int64_t pend_j[kDefer];
-  int pend_delta[kDefer];
-  int npend = 0;
-  auto finish = [&](uint4 v, int64_t jj, int delta) {
-    const uint32_t cc = fallback_requant(v, delta, packed + jj * 16);
-    if (cc != 0x0101u) *reinterpret_cast<uint16_t*>(codes + 2 * jj) = (uint16_t)cc;
-    ++nfb;
-  };
-  auto finish_pending = [&]() {
-#pragma unroll
-    for (int q = 0; q < kDefer; ++q)
-      if (q < npend) finish(pend_v[q], pend_j[q], pend_delta[q]);
-    npend = 0;
+  // a fallback block: listed, or (list full) requantized here
+  const bool listable = per_group <= 0xFFFFFFFFll;       // list entries hold 32-bit block indices
+  auto fallback_block_at = [&](int64_t jg, int delta) {
+    const uint32_t slot = listable ? atomicAdd(&fb_n, 1u) : (uint32_t)kFbCap;
+    if (slot < (uint32_t)kFbCap) {
+      fb_j[slot] = (uint32_t)(jg - base);
+      fb_d[slot] = (uint8_t)delta;
+    } else {
+      const uint32_t cc = fallback_requant(*reinterpret_cast<const uint4*>(packed + jg * 16), delta, packed + jg * 16);
+      if (cc != 0x0101u) *reinterpret_cast<uint16_t*>(codes + 2 * jg) = (uint16_t)cc;
+      ++nfb;
+    }
   };
   int64_t c0 = (int64_t)blockIdx.x * kCodesChunk;
   auto whole = [&](int64_t c) { return aligned && c + kCodesChunk <= per_group; };
@@ -241,53 +230,48 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
         c[2 * w + 1] = cw[2] | (cw[3] << 16);
       }
       *reinterpret_cast<uint4*>(codes + 2 * j) = make_uint4(c[0], c[1], c[2], c[3]);
-      // this step's fallbacks: loads now, the work next step (or now, past kDefer)
-      uint4 new_v[kDefer];
-      int64_t new_j[kDefer];
-      int new_delta[kDefer];
-      int nnew = 0;
       if (fbmask) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if ((fbmask >> i) & 1u) {
-            const int delta = km - (int32_t)((ew[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-            if (nnew < kDefer) {
-#pragma unroll
-              for (int q = 0; q < kDefer; ++q) {
-                if (q == nnew) {
-                  new_v[q] = *reinterpret_cast<const uint4*>(packed + (j + i) * 16);
-                  new_j[q] = j + i;
-                  new_delta[q] = delta;
-                }
-              }
-              ++nnew;
-            } else {
-              finish(*reinterpret_cast<const uint4*>(packed + (j + i) * 16), j + i, delta);
-            }
-          }
-        }
+        for (int i = 0; i < 8; ++i)
+          if ((fbmask >> i) & 1u) fallback_block_at(j + i, km - (int32_t)((ew[i >> 2] >> (8 * (i & 3))) & 0xFFu));
       }
-      finish_pending();
-#pragma unroll
-      for (int q = 0; q < kDefer; ++q) {
-        pend_v[q] = new_v[q];
-        pend_j[q] = new_j[q];
-        pend_delta[q] = new_delta[q];
-      }
-      npend = nnew;
     } else {
       const int64_t c1 = c0 + kCodesChunk < per_group ? c0 + kCodesChunk : per_group;
       for (int64_t u = c0 + threadIdx.x; u < c1; u += kThreads) {
         const int64_t j = base + u;
-        const uint32_t cc = mx_block_codes(e8m0[j], km, packed + j * 16, nfb);
+        const uint32_t b = e8m0[j];
+        uint32_t cc = tab[b];
+        if (cc == kFallback) {
+          fallback_block_at(j, km - (int32_t)b);
+          cc = 0x0101u;
+        }
         codes[2 * j] = (uint8_t)(cc & 0xFFu);
         codes[2 * j + 1] = (uint8_t)(cc >> 8);
       }
     }
   }
-  finish_pending();
+  // the listed fallback blocks, four per thread per round, loads first
+  __syncthreads();
+  const int nl = (int)(fb_n < (uint32_t)kFbCap ? fb_n : (uint32_t)kFbCap);
+  for (int r0 = 0; r0 < nl; r0 += 4 * kThreads) {
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s = r0 + q * kThreads + threadIdx.x;
+      if (s < nl) v[q] = *reinterpret_cast<const uint4*>(packed + (base + fb_j[s]) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s = r0 + q * kThreads + threadIdx.x;
+      if (s < nl) {
+        const int64_t jg = base + fb_j[s];
+        const uint32_t cc = fallback_requant(v[q], (int)fb_d[s], packed + jg * 16);
+        if (cc != 0x0101u) *reinterpret_cast<uint16_t*>(codes + 2 * jg) = (uint16_t)cc;
+        ++nfb;
+      }
+    }
+  }
   if (fallback) {
-    __shared__ int part[kThreads / 64];
     int v = nfb;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -309,6 +293,10 @@ int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t
   // workgroups per group: about kCastWgs in all, at most one per step; the
   // pass-1 partials (int16, one per workgroup) fit in the group's 2*per_group
   // code bytes since nx <= per_group
+  if (per_group == 0) {                               // no rows: scale_2 = 2^-8, no fallback blocks
+    cast_scale_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(nullptr, 0, 0, groups, scale2, fallback);
+    return launch_status("cast_scale_kernel");
+  }
   int64_t want = (kCastWgs + groups - 1) / groups;
   int64_t nx1 = (per_group + kKmaxChunk - 1) / kKmaxChunk;
   if (nx1 > want) nx1 = want;

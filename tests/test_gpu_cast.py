@@ -77,3 +77,32 @@ def test_cast_subnormal_tensor_scale():
         e8[i] = rng.integers(0, i + 1, (m, r, k // 32))   # k_max code <= i
         e8[i, 0, 0, 0] = i
     _check(packed, e8)
+
+
+def test_cast_empty_rows():
+    """Groups with no rows: no exponent, so scale_2 = 2^-8 (k_max taken as 0),
+    no fallback blocks, nothing else written."""
+    note("cast rows == 0")
+    g, m, k = 3, 2, 64
+    packed = np.zeros((g, m, 0, k // 2), np.uint8)
+    e8 = np.zeros((g, m, 0, k // 32), np.uint8)
+    _check(packed, e8)
+
+
+def test_cast_several_slices_ragged():
+    """A group of 134,400 exponents: three workgroup slices of 44,800 bytes,
+    ragged against the 4 KiB units of a workgroup's loads."""
+    note("cast three slices per group")
+    packed, e8, forced = datagen.config5(seed=5, experts=2, rows=300, k=7168, forced_frac=0.01)
+    fb = _check(packed, e8)
+    assert np.array_equal(fb, forced.reshape(2, -1).sum(axis=1))
+
+
+def test_cast_many_fallbacks_per_lane():
+    """Most blocks out of the window: lanes with more than four fallback
+    blocks take the one-by-one path."""
+    note("cast many fallbacks per lane")
+    packed, e8, forced = datagen.config5(seed=6, experts=2, rows=64, k=2048, forced_frac=0.7)
+    fb = _check(packed, e8)
+    assert np.array_equal(fb, forced.reshape(2, -1).sum(axis=1))
+    assert fb.min() > 0.5 * 64 * 2 * (2048 // 32)
