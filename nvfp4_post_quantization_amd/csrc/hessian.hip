@@ -341,8 +341,7 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
   q.s2 = *scale2;
   q.inv = (float)(1.0 / (6.0 * (double)q.s2));
   q.est = q.inv > 0.0f && q.inv < __builtin_inff();
-  build_code_search(tp, q.s2);
-  build_code_tables(t, q.s2, force_exact);                 // syncs
+  build_all_tables(tp, t, q.s2, force_exact);                 // syncs
   const int mode = table_mode(t);
   u16x2 amx;
   if (mode == 0)

@@ -182,7 +182,7 @@ __device__ __forceinline__ bool cert_code(float d, float r, float rl, int level)
 // since the lanes of a wave quantize at different codes).  Test hook:
 // force_exact = 1 uses the exact thresholds only, 2 skips level 0, 3 skips
 // levels 0 and 1.
-__device__ inline void build_code_tables(CodeTables& t, float s2, int force_exact) {
+__device__ __forceinline__ void build_code_tables(CodeTables& t, float s2, int force_exact) {
   const int c = threadIdx.x;
   if (c < 4) { t.cert[c] = 0u; t.cert1[c] = 0u; t.cert2[c] = 0u; }
   __syncthreads();
@@ -333,9 +333,8 @@ __device__ __forceinline__ float e2m1_mag(int idx) {
 // S), ties going to the even code.  mid * S is exact in double (a midpoint has
 // at most 5 significant bits, S at most 26).  tp[126] is a sentinel that no
 // pattern passes (saturation at 448).
-__device__ inline void build_e4m3_thresholds(int32_t* tp, double S) {
-  int c = threadIdx.x;
-  if (c < 128) {
+__device__ __forceinline__ void build_e4m3_thresholds(int32_t* tp, double S, int c = threadIdx.x) {
+  if (c >= 0 && c < 128) {
     int32_t t = 0x7FFFFFFF;
     if (c < kCodes - 1) {
       double mid = 0.5 * ((double)e4m3_value(c) + (double)e4m3_value(c + 1));
@@ -352,6 +351,15 @@ __device__ inline void build_e4m3_thresholds(int32_t* tp, double S) {
 // Thresholds of the block-code search: the block code is the E4M3 encode of
 // the block max over 6 * scale_2 (exact in double).
 __device__ inline void build_code_search(int32_t* tp, float s2) { build_e4m3_thresholds(tp, 6.0 * (double)s2); }
+
+// Both tables of a workgroup of at least 256 threads: the block-code
+// thresholds on threads 128..255 while threads 0..127 certify the E2M1 paths
+// (that certification is the longer part; run one after the other they had
+// cost about 4 us at the start of every launch).  Syncs before returning.
+__device__ __forceinline__ void build_all_tables(int32_t* tp, CodeTables& t, float s2, int force_exact) {
+  build_e4m3_thresholds(tp, 6.0 * (double)s2, (int)threadIdx.x - 128);
+  build_code_tables(t, s2, force_exact);
+}
 
 // E4M3 code estimate of pattern P over the thresholds' scale S, for
 // 0 < inv = RN_f32(1 / S) < inf: the FP32 quotient P * inv is within 2^-23

@@ -363,8 +363,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
   __shared__ uint32_t st_done[kStageBatches];
   const float s2 = *scale2;
   if (threadIdx.x < kStageBatches) st_done[threadIdx.x] = 0u;
-  build_code_search(tp, s2);
-  build_code_tables(t, s2, force_exact);                     // syncs
+  build_all_tables(tp, t, s2, force_exact);                     // syncs
   const int mode = table_mode(t);
 
   const int64_t groups = k >> 4;
@@ -473,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const uint16_t* __re
     const uint32_t nw = (uint32_t)(groups - g0 < kWaves ? groups - g0 : kWaves);
     const int nbat = (int)((r1 - r0 + 63) >> 6);
     if (j == nbat - 1 && prev + 1 == nw) {
-      __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       // whole-row-segment stores where the destinations allow them (uniform)
       const bool nib16 = nw == kWaves && ((k >> 1) % 16) == 0 && (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
       const bool code4 = nw == kWaves && (groups % 4) == 0 && (reinterpret_cast<uintptr_t>(codes) & 3) == 0;

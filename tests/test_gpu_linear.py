@@ -56,7 +56,8 @@ def test_fakequant_tensors(path, which):
 
 
 @pytest.mark.parametrize("rows,k,ld,ldo,factor", [(1, 16, None, None, 1.0), (333, 48, 56, 64, 1.0),
-                                                  (65, 272, None, 280, 1 / 64), (100, 64, None, None, 4096.0)])
+                                                  (65, 272, None, 280, 1 / 64), (100, 64, None, None, 4096.0),
+                                                  (9, 1024, 1040, 1048, 1.0), (130, 3072, None, 3080, 1 / 64)])
 def test_fakequant_ragged_strided_scales(rows, k, ld, ldo, factor):
     note(f"fakequant rows={rows} k={k} ld={ld} ldo={ldo} x{factor}")
     rng = np.random.default_rng(rows + k)

@@ -87,7 +87,9 @@ def test_quantize_config3_full(path):
 
 
 @pytest.mark.parametrize("rows,k,ld", [(1, 16, None), (3, 48, None), (5, 4112, None), (7, 64, 72),
-                                       (300, 272, 288), (2, 8192, None)])
+                                       (300, 272, 288), (2, 8192, None),
+                                       # whole 64-block units per row (the unit kernel): strided, few units
+                                       (3, 1024, 1032), (37, 2048, 2056)])
 def test_quantize_ragged(rows, k, ld, path):
     note(f"quantize_dynamic rows={rows} k={k} ld={ld} ({path})")
     rng = np.random.default_rng(rows * 131 + k)
