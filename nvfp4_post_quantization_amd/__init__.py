@@ -27,7 +27,9 @@ __all__ = [
     "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward", "scale_sweep_stats",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
+# NVFP4MI_LIB names another build of the same library (the host-sanitizer
+# build of tests/test_abi_sanitized.py); by default the in-tree build.
+LIB_PATH = os.environ.get("NVFP4MI_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4mi.so")
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64

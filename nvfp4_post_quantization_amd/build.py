@@ -69,5 +69,49 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-sanitizer build of the argument-validation layer: api.hip compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer on its host code only
+# (-Xarch_host before each -fsanitize=; device code is built as usual), linked
+# with the other objects of the regular build.  Loaded with the clang ASan
+# runtime preloaded; tests/test_abi_sanitized.py runs the C-ABI validation
+# tests against it.  No GPU is needed: validation fails before any HIP call.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "san", "libnvfp4mi_san.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that the sanitized library needs preloaded."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "llvm", "bin", "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang ASan runtime not found")
+    return path
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build SAN_LIB (the regular objects must exist: build() first)."""
+    others = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.hip"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"regular objects missing ({missing[0]}): run build() first")
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    obj = os.path.join(os.path.dirname(SAN_LIB), "api_san.o")
+    cmds = [
+        [_hipcc(), *[f for f in FLAGS if f != "-O3"], "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, "api.hip"),
+         "-o", obj],
+        [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *others, "-o", SAN_LIB,
+         "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *LINK],
+    ]
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build failed:\n{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
