@@ -224,17 +224,20 @@ def main():
 
     def step(ev, b, wait_ev):
         """The timed step, on buffer set b (H, amax and scale_2 alternate
-        between consecutive steps).  The first HIP stream accumulates both
-        calibration streams' H; the second takes a1 and a4-a6, the gate/up
-        sweeps once the first H is done and the down sweep once the second
-        is, every sweep capped at one workgroup per CU.  So the down sweep of
-        one step runs beside the next step's first Hessian; wait_ev (the
-        second stream's end of the step two back, the last reader of set b)
-        guards the reuse of set b."""
+        between consecutive steps).  The first HIP stream runs a1 and a4-a6,
+        then accumulates both calibration streams' H; the second takes the
+        gate/up sweeps once the first H is done and the down sweep once the
+        second is, every sweep capped at one workgroup per CU.  So the down
+        sweep of one step runs beside the next step's a1-a6 and first
+        Hessian; wait_ev (the second stream's end of the step two back, the
+        last reader of set b) guards the reuse of set b.  The HBM-bound
+        stages a1-a6 run in series with the HBM-bound accumulate rather than
+        beside it: measured on MI355X, beside it they slowed its calls by
+        about as much as their own time, for the same step time."""
         ev["start"].record(stream)
-        stage_calls("a1_scale2", sptr_b, b)
+        stage_calls("a1_scale2", sptr, b)
         for k in ("a4_quantize", "a5_dequant", "a6_restore", "a6_cast"):
-            stage_calls(k, sptr_b)
+            stage_calls(k, sptr)
         if wait_ev is not None:
             stream.wait_event(wait_ev)
         for s in (0, 1):
@@ -374,7 +377,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "per_launch": f"{x_bytes / 32 / 1e9:.4f} GB avg, {per_launch_s * 1e3:.4f} ms avg (events around "
                               f"each calibration stream's 16 calls, on their stream, in the timed steps, where they "
-                              f"share the GPU with the side-stream sweeps)",
+                              f"share the GPU with the second stream's sweeps)",
                 "alone": {"ms_per_launch": round(h_call_serial_ms, 4), "achieved": round(alone, 1),
                           "frac": round(alone / HBM_PEAK_GBS, 4),
                           "note": "the same calls in the serial pass, with nothing else running"}}
@@ -607,11 +610,11 @@ def main():
             "calibration_tokens": datagen.C4_TOKENS,
             "chunk_tokens": datagen.C4_CHUNK,
             "parallelism": "single GPU",
-            "schedule": "timed steps: a2 of both calibration streams on one HIP stream; a1, a4-a6 and the three "
-                        "sweeps (capped at one workgroup per CU) on a second stream, the gate/up sweeps beside the "
-                        "second calibration stream's Hessian and the down sweep beside the next step's first "
-                        "(two alternating sets of H/amax/scale_2 buffers; checked bit-exact against the serial "
-                        "order); stages: the same work in stage order on one stream",
+            "schedule": "timed steps: a1, a4-a6 and then a2 of both calibration streams on one HIP stream; the "
+                        "three sweeps (capped at one workgroup per CU) on a second stream, the gate/up sweeps beside "
+                        "the second calibration stream's Hessian and the down sweep beside the next step's a1-a6 and "
+                        "first Hessian (two alternating sets of H/amax/scale_2 buffers; checked bit-exact against "
+                        "the serial order); stages: the same work in stage order on one stream",
             "serial_step_ms": round(step_ms, 4),
         },
         "roofline": roof,

@@ -36,9 +36,12 @@ namespace {
 constexpr int kThreads = 256;
 static_assert(kThreads == 256, "the code table of pass 3 takes one entry per thread");
 
-constexpr int kCastWgs = 2048;                          // workgroups per pass, spread over the groups
-constexpr int64_t kKmaxChunk = 16 * kThreads * 4;       // E8M0 bytes per workgroup step: 4 x 16 B per thread
-constexpr int64_t kCodesChunk = 8 * kThreads;           // MX blocks per workgroup step: 8 per thread
+constexpr int kKmaxWgs = 4096;                          // pass-1 workgroups, spread over the groups
+constexpr int kCodesWgs = 2048;                         // pass-3 workgroups, spread over the groups
+constexpr int kKmaxLoads = 8;                          // 16-byte loads in flight per thread in pass 1
+constexpr int64_t kKmaxChunk = 16 * kThreads * kKmaxLoads;   // E8M0 bytes per workgroup step
+constexpr int kCodesSub = 4;                            // 8-byte exponent loads per thread per pass-3 step
+constexpr int64_t kCodesChunk = 8 * kThreads * kCodesSub;    // MX blocks per workgroup step
 
 // Largest valid code (!= 255) among 16 E8M0 bytes, or -1.
 __device__ __forceinline__ int32_t max_valid16(const uint4& v) {
@@ -69,11 +72,11 @@ __global__ __launch_bounds__(kThreads) void cast_kmax_kernel(const uint8_t* __re
   int32_t m = -1;
   for (int64_t c0 = (int64_t)blockIdx.x * kKmaxChunk; c0 < per_group; c0 += nx * kKmaxChunk) {
     if (aligned && c0 + kKmaxChunk <= per_group) {
-      uint4 v[4];
+      uint4 v[kKmaxLoads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ld_nt4(e + c0 + 16 * (threadIdx.x + kThreads * u));
+      for (int u = 0; u < kKmaxLoads; ++u) v[u] = ld_nt4(e + c0 + 16 * (threadIdx.x + kThreads * u));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) m = max(m, max_valid16(v[u]));
+      for (int u = 0; u < kKmaxLoads; ++u) m = max(m, max_valid16(v[u]));
     } else {
       const int64_t c1 = c0 + kKmaxChunk < per_group ? c0 + kKmaxChunk : per_group;
       for (int64_t q = c0 + threadIdx.x; q < c1; q += kThreads) {
@@ -143,13 +146,17 @@ __device__ __forceinline__ uint32_t fallback_requant(uint4 v, int delta, uint8_t
   return codes;
 }
 
-// Pass 3: workgroup (x, g) takes steps x, x + nx, ... of group g; a thread
-// takes 8 consecutive MX blocks (one 8-byte E8M0 load, one 16-byte code
-// store, so each wave instruction covers one contiguous run) where the step is
-// 8-aligned and whole, single blocks otherwise.  The code pair of an E8M0 byte
-// depends only on it and the group's k_max, so the workgroup first tabulates
-// all 256 bytes in LDS (kFallback marks a block outside the window); the next
-// step's exponents are loaded before the current step is coded.
+// Pass 3: workgroup (x, g) takes steps x, x + nx, ... of group g.  Where the
+// step is 8-aligned and whole, a thread codes kCodesSub runs of 8 consecutive
+// MX blocks, kThreads * 8 blocks apart (per run one 8-byte E8M0 load and one
+// 16-byte code store, so each wave instruction covers one contiguous span),
+// with the next step's exponents loaded before the current step is coded:
+// 32-64 bytes of loads in flight per thread (measured: with one run per step
+// the pass was latency-bound).  Other steps go block by block.  The code pair
+// of an E8M0 byte depends only on it and the group's k_max, so the workgroup
+// first tabulates all 256 bytes in LDS (kFallback marks a block outside the
+// window).  Codes go out with non-temporal stores (measured on MI355X: 139 ->
+// 115 us for the MoE expert set, MALL defeated; fewer workgroups were slower).
 // Fallback blocks are rare and scattered.  A step stores the usual fallback
 // code pair 0x0101 as a placeholder and appends the block to a list in LDS;
 // after its last step the workgroup requantizes the whole list at once, each
@@ -206,34 +213,44 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
   };
   int64_t c0 = (int64_t)blockIdx.x * kCodesChunk;
   auto whole = [&](int64_t c) { return aligned && c + kCodesChunk <= per_group; };
-  uint2 e = make_uint2(0u, 0u);
-  if (c0 < per_group && whole(c0)) e = ld_nt2(e8m0 + base + c0 + 8 * threadIdx.x);
+  // sub-step u of a step: 8 consecutive blocks per thread at c + 8 * (threadIdx.x + kThreads * u)
+  uint2 e[kCodesSub];
+  auto load_step = [&](int64_t c) {
+#pragma unroll
+    for (int u = 0; u < kCodesSub; ++u) e[u] = ld_nt2(e8m0 + base + c + 8 * (threadIdx.x + kThreads * u));
+  };
+  if (c0 < per_group && whole(c0)) load_step(c0);
   for (; c0 < per_group; c0 += step) {
     if (whole(c0)) {
-      const uint2 cur = e;
+      uint2 cur[kCodesSub];
+#pragma unroll
+      for (int u = 0; u < kCodesSub; ++u) cur[u] = e[u];
       const int64_t n0 = c0 + step;
-      if (n0 < per_group && whole(n0)) e = ld_nt2(e8m0 + base + n0 + 8 * threadIdx.x);
-      const int64_t j = base + c0 + 8 * threadIdx.x;
-      const uint32_t ew[2] = {cur.x, cur.y};
-      uint32_t c[4];
-      uint32_t fbmask = 0;
+      if (n0 < per_group && whole(n0)) load_step(n0);
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        uint32_t cw[4];
+      for (int u = 0; u < kCodesSub; ++u) {
+        const int64_t j = base + c0 + 8 * (threadIdx.x + kThreads * u);
+        const uint32_t ew[2] = {cur[u].x, cur[u].y};
+        uint32_t c[4];
+        uint32_t fbmask = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cw[i] = tab[(ew[w] >> (8 * i)) & 0xFFu];
-          fbmask |= (cw[i] == kFallback ? 1u : 0u) << (4 * w + i);
-          cw[i] = cw[i] == kFallback ? 0x0101u : cw[i];
+        for (int w = 0; w < 2; ++w) {
+          uint32_t cw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            cw[i] = tab[(ew[w] >> (8 * i)) & 0xFFu];
+            fbmask |= (cw[i] == kFallback ? 1u : 0u) << (4 * w + i);
+            cw[i] = cw[i] == kFallback ? 0x0101u : cw[i];
+          }
+          c[2 * w] = cw[0] | (cw[1] << 16);
+          c[2 * w + 1] = cw[2] | (cw[3] << 16);
         }
-        c[2 * w] = cw[0] | (cw[1] << 16);
-        c[2 * w + 1] = cw[2] | (cw[3] << 16);
-      }
-      *reinterpret_cast<uint4*>(codes + 2 * j) = make_uint4(c[0], c[1], c[2], c[3]);
-      if (fbmask) {
+        st_nt4(codes + 2 * j, make_uint4(c[0], c[1], c[2], c[3]));
+        if (fbmask) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if ((fbmask >> i) & 1u) fallback_block_at(j + i, km - (int32_t)((ew[i >> 2] >> (8 * (i & 3))) & 0xFFu));
+          for (int i = 0; i < 8; ++i)
+            if ((fbmask >> i) & 1u) fallback_block_at(j + i, km - (int32_t)((ew[i >> 2] >> (8 * (i & 3))) & 0xFFu));
+        }
       }
     } else {
       const int64_t c1 = c0 + kCodesChunk < per_group ? c0 + kCodesChunk : per_group;
@@ -290,18 +307,19 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
 int launch_mx_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, int64_t mats, int64_t rows, int64_t k,
                    uint8_t* codes, float* scale2, int64_t* fallback, hipStream_t s) {
   const int64_t per_group = mats * rows * (k / 32);   // MX blocks (= E8M0 bytes) per group; k % 32 == 0
-  // workgroups per group: about kCastWgs in all, at most one per step; the
+  // workgroups per group: about kCodesWgs (kKmaxWgs) in all, at most one per step; the
   // pass-1 partials (int16, one per workgroup) fit in the group's 2*per_group
   // code bytes since nx <= per_group
   if (per_group == 0) {                               // no rows: scale_2 = 2^-8, no fallback blocks
     cast_scale_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(nullptr, 0, 0, groups, scale2, fallback);
     return launch_status("cast_scale_kernel");
   }
-  int64_t want = (kCastWgs + groups - 1) / groups;
+  const int64_t want1 = (kKmaxWgs + groups - 1) / groups;
+  const int64_t want3 = (kCodesWgs + groups - 1) / groups;
   int64_t nx1 = (per_group + kKmaxChunk - 1) / kKmaxChunk;
-  if (nx1 > want) nx1 = want;
+  if (nx1 > want1) nx1 = want1;
   int64_t nx3 = (per_group + kCodesChunk - 1) / kCodesChunk;
-  if (nx3 > want) nx3 = want;
+  if (nx3 > want3) nx3 = want3;
   int16_t* partial = reinterpret_cast<int16_t*>(codes);
   const int64_t stride16 = per_group;                 // int16 slots per group = 2*per_group bytes
   int st;

@@ -67,6 +67,11 @@ __device__ __forceinline__ uint2 ld_nt2(const void* p) {
   const ntu32x2 v = __builtin_nontemporal_load(reinterpret_cast<const ntu32x2*>(p));
   return make_uint2(v.x, v.y);
 }
+// Non-temporal 16-byte store (streamed output that nothing reads back soon).
+__device__ __forceinline__ void st_nt4(void* p, uint4 v) {
+  const ntu32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<ntu32x4*>(p));
+}
 
 // Two fp32 -> two FP4 codes in byte `sel` of `old` (element a in the low nibble).
 template <int SEL>
