@@ -67,11 +67,20 @@ __device__ __forceinline__ uint2 ld_nt2(const void* p) {
   const ntu32x2 v = __builtin_nontemporal_load(reinterpret_cast<const ntu32x2*>(p));
   return make_uint2(v.x, v.y);
 }
-// Non-temporal 16-byte store (streamed output that nothing reads back soon).
+// Non-temporal stores (streamed output that nothing reads back soon).  They
+// pay off where one wave store instruction covers a contiguous span (16, 8 or
+// 1 bytes per lane, lanes adjacent); measured on MI355X, kernels whose lanes
+// write 32 bytes each as two interleaved 16-byte stores ran up to twice as
+// slow with them, so those keep ordinary stores.
 __device__ __forceinline__ void st_nt4(void* p, uint4 v) {
   const ntu32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<ntu32x4*>(p));
 }
+__device__ __forceinline__ void st_nt2(void* p, uint2 v) {
+  const ntu32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<ntu32x2*>(p));
+}
+__device__ __forceinline__ void st_nt1(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
 
 // Two fp32 -> two FP4 codes in byte `sel` of `old` (element a in the low nibble).
 template <int SEL>

@@ -240,8 +240,8 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
           dst[0] = dequant_word(q.x, d);
           dst[1] = dequant_word(q.y, d);
         } else {
-          *reinterpret_cast<uint2*>(packed + pos.r * (k >> 1) + pos.g * 8) = q;
-          codes[pos.r * nb + pos.g] = (uint8_t)c;
+          st_nt2(packed + pos.r * (k >> 1) + pos.g * 8, q);
+          st_nt1(codes + pos.r * nb + pos.g, (uint8_t)c);
         }
       }
       pos.advance(dr, dg, nb);
@@ -333,8 +333,8 @@ __global__ __launch_bounds__(256) void quantize_units_kernel(const uint16_t* __r
           dst[0] = dequant_word(qn.x, d);
           dst[1] = dequant_word(qn.y, d);
         } else {
-          *reinterpret_cast<uint2*>(packed + r * (k >> 1) + g * 8) = qn;
-          codes[r * nb + g] = (uint8_t)c;
+          st_nt2(packed + r * (k >> 1) + g * 8, qn);
+          st_nt1(codes + r * nb + g, (uint8_t)c);
         }
       }
     }
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
       if (pos.r < rows) {
-        *reinterpret_cast<uint4*>(out + pos.r * k + pos.g * 8) = dequant_word(pc[j], dt[cc[j]]);
+        st_nt4(out + pos.r * k + pos.g * 8, dequant_word(pc[j], dt[cc[j]]));
       }
       pos.advance(dr, dg, nh);
     }
