@@ -695,14 +695,27 @@ def sweep_work(lib, chk, w, H, s2, ref_out, sptr):
     return [int(v) for v in st.cpu().tolist()]
 
 
+# the sources each profiled kernel is built from; a committed counter line
+# applies while their hashes (first 16 hex digits of sha256, joined by "+")
+# match the ones it was taken on
+KERNEL_SOURCES = {
+    "sweep_kernel": ("sweep_kernel.hpp", "sweep.hip", "nvfp4_device.hpp", "common.hpp"),
+    "hessian_partial_kernel": ("hessian.hip", "nvfp4_device.hpp", "common.hpp"),
+    "hessian_reduce_kernel": ("hessian.hip", "nvfp4_device.hpp", "common.hpp"),
+}
+
+
+def src_sha(files):
+    csrc = os.path.join(ROOT, "nvfp4_post_quantization_amd", "csrc")
+    return "+".join(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16] for f in files)
+
+
 def valu_issue_from_profiles():
     """VALU issue utilisation of the uncapped sweep from the committed SQ
     counter summary, if it was taken on the current sweep sources."""
     path = os.path.join(ROOT, "profiles", "sweep_valu_counters.txt")
     try:
-        csrc = os.path.join(ROOT, "nvfp4_post_quantization_amd", "csrc")
-        sha = "+".join(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
-                       for f in ("sweep.hip", "nvfp4_device.hpp"))
+        sha = src_sha(KERNEL_SOURCES["sweep_kernel"])
         for ln in open(path):
             if ln.startswith("kernel=sweep_kernel"):
                 kv = dict(x.split("=", 1) for x in ln.split() if "=" in x)
@@ -855,15 +868,12 @@ def traffic_from_profiles(kernel: str):
     probe) from the committed counter summary; null unless every kernel of
     `kernel` ("a+b" sums them) was measured on its current source."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
-    srcs = {"sweep_kernel": "sweep.hip", "hessian_partial_kernel": "hessian.hip",
-            "hessian_reduce_kernel": "hessian.hip"}
     total = 0.0
     try:
         lines = [dict(kv.split("=", 1) for kv in ln.split() if "=" in kv)
                  for ln in open(path) if ln.startswith("kernel=")]
         for name in kernel.split("+"):
-            src = os.path.join(ROOT, "nvfp4_post_quantization_amd", "csrc", srcs[name])
-            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            sha = src_sha(KERNEL_SOURCES[name])
             hit = [f for f in lines if f.get("kernel") == name and f.get("src_sha") == sha]
             if not hit:
                 return None

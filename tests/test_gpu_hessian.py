@@ -100,3 +100,35 @@ def test_hessian_wide_k_ranges_cross_slabs(t, k):
     rng = np.random.default_rng(t + k)
     x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (t, k)).astype(np.float32))
     _check(x)
+
+
+@pytest.mark.parametrize("fill", ["zero", "ones", "random"])
+def test_hessian_workspace_contents_do_not_matter(fill):
+    """Any workspace contents give the same H, bit for bit, call after call on
+    one workspace (the W4A4 variant's calls in between): every partial slot
+    the reduce reads is written earlier in the same call."""
+    note(f"hessian workspace contents: {fill}")
+    rng = np.random.default_rng(21)
+    shapes = [(3000, 1024), (130, 66048), (4096, 2048)]
+    xs = [to_dev_bf16(datagen.f32_to_bf16_bits(rng.laplace(0, 1, s).astype(np.float32))) for s in shapes]
+    need = max(nq.hessian_workspace_bytes(*s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    if fill == "ones":
+        ws.fill_(0xFF)
+    elif fill == "random":
+        ws.copy_(torch.from_numpy(rng.integers(0, 256, need, dtype=np.uint8)))
+    s2 = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    for rep in range(2):
+        for x in xs:
+            k = x.shape[1]
+            ref = torch.zeros((k // 16, 16, 16), dtype=torch.float32, device=DEV)
+            nq.hessian_accum(x, ref)                                # its own fresh workspace
+            ref_fq = torch.zeros_like(ref)
+            nq.hessian_accum_fq(x, s2, ref_fq)
+            h = torch.zeros_like(ref)
+            nq.hessian_accum(x, h, workspace=ws)
+            h_fq = torch.zeros_like(ref)
+            nq.hessian_accum_fq(x, s2, h_fq, workspace=ws)
+            h2 = torch.zeros_like(ref)
+            nq.hessian_accum(x, h2, workspace=ws)
+            assert torch.equal(h, ref) and torch.equal(h2, ref) and torch.equal(h_fq, ref_fq)
