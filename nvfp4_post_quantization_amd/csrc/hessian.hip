@@ -46,7 +46,6 @@ constexpr int kTile = 64;                 // tokens per LDS tile
 constexpr int kThreads = 256;
 constexpr int kTargetWgs = 512;           // two workgroups on each of 256 CUs (measured best)
 constexpr int kTargetWgsFq = 1024;        // fake-quant variant: ALU-heavier, four per CU hide more latency
-constexpr int kReduceParts = 4;           // workgroup sub-ranges summed in parallel by the reduce
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
@@ -354,68 +353,56 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
 }
 
 // H[g] += sum of the partials of group g over the workgroups whose range
-// touches g's slab, in fp64 and in workgroup order (deterministic).  One
-// workgroup per group: thread t sums float4 t%64 of the group over the t/64-th
-// of the owning workgroups; the kReduceParts sums are then added in order.
+// touches g's slab, in fp64 and in workgroup order (deterministic).  One wave
+// per group (four groups per workgroup): lane e sums float4 e of the group
+// over every owning workgroup, its H element loaded up front, so the kernel
+// is one round of loads (it sits between two accumulate passes, where its
+// latency is what counts).
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __restrict__ ws, int64_t tiles,
-                                                              int64_t total, int64_t wgs, int64_t segs,
+                                                              int64_t total, int64_t wgs, int64_t segs, int64_t groups,
                                                               float4* __restrict__ H) {
-  __shared__ double part[kReduceParts][64][4];
-  const int64_t g = blockIdx.x;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= groups) return;
   const int64_t s = g / kSlabGroups;
   const int gl = (int)(g % kSlabGroups);
   const int e = threadIdx.x & 63;
-  const int c = threadIdx.x >> 6;
-  // owning workgroups of slab s: w_lo .. w_hi (all with non-empty ranges)
+  float4 h = H[g * 64 + e];
+  // owning workgroups of slab s: w_lo .. w_hi (all with non-empty ranges);
+  // only w_lo's range can start before slab s, so only its slot for s can
+  // sit past segment 0
   const int64_t w_lo = cdiv((s * tiles + 1) * wgs, total) - 1;
   const int64_t w_hi = cdiv((s + 1) * tiles * wgs, total) - 1;
-  const int64_t n = w_hi - w_lo + 1;
-  const int64_t a = w_lo + n * c / kReduceParts;
-  const int64_t b = w_lo + n * (c + 1) / kReduceParts;
+  const int n = (int)(w_hi - w_lo + 1);
+  const int seg_lo = (int)(s - (w_lo * total / wgs) / tiles);
+  const int sg = (int)segs;
+  const float4* p0 = ws + ((w_lo * segs + seg_lo) * kSlabGroups + gl) * 64 + e;
+  auto at = [&](int i) -> float4 { return p0[(int64_t)(i * sg - (i ? seg_lo : 0)) * (kSlabGroups * 64)]; };
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  auto at = [&](int64_t w) -> float4 {
-    const int64_t seg = s - (w * total / wgs) / tiles;
-    return ws[((w * segs + seg) * kSlabGroups + gl) * 64 + e];
-  };
-  int64_t w = a;
-  for (; w + 8 <= b; w += 8) {
-    float4 v[8];
+  int i = 0;
+  for (; i + 16 <= n; i += 16) {
+    float4 v[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = at(w + j);
+    for (int j = 0; j < 16; ++j) v[j] = at(i + j);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
       s0 += (double)v[j].x;
       s1 += (double)v[j].y;
       s2 += (double)v[j].z;
       s3 += (double)v[j].w;
     }
   }
-  for (; w < b; ++w) {
-    const float4 v = at(w);
+  for (; i < n; ++i) {
+    const float4 v = at(i);
     s0 += (double)v.x;
     s1 += (double)v.y;
     s2 += (double)v.z;
     s3 += (double)v.w;
   }
-  part[c][e][0] = s0;
-  part[c][e][1] = s1;
-  part[c][e][2] = s2;
-  part[c][e][3] = s3;
-  __syncthreads();
-  if (c == 0) {
-    double t[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int p = 0; p < kReduceParts; ++p) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] += part[p][e][r];
-    }
-    float4 h = H[g * 64 + e];
-    h.x = (float)((double)h.x + t[0]);
-    h.y = (float)((double)h.y + t[1]);
-    h.z = (float)((double)h.z + t[2]);
-    h.w = (float)((double)h.w + t[3]);
-    H[g * 64 + e] = h;
-  }
+  h.x = (float)((double)h.x + s0);
+  h.y = (float)((double)h.y + s1);
+  h.z = (float)((double)h.z + s2);
+  h.w = (float)((double)h.w + s3);
+  H[g * 64 + e] = h;
 }
 
 }  // namespace
@@ -430,8 +417,10 @@ size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
 }
 
 static int launch_reduce(const Plan& p, int64_t k, const float* ws, float* H, hipStream_t s) {
-  hessian_reduce_kernel<<<(unsigned)(k / 16), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles, p.total,
-                                                            p.wgs, p.segs, reinterpret_cast<float4*>(H));
+  const int64_t groups = k / 16;
+  hessian_reduce_kernel<<<(unsigned)((groups + 3) / 4), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles,
+                                                                      p.total, p.wgs, p.segs, groups,
+                                                                      reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
 }
 

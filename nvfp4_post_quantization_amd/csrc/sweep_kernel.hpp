@@ -82,10 +82,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kPruneMargin = 2e-5f;
-// Workgroups per launch (C4, same process: 2048 against 4096 took the down
-// sweep from 0.905 to 0.81 ms and the gate sweep from 0.873 to 0.838 ms, half
-// the per-workgroup set-up; 1024 leaves too little to balance when capped).
+// Target workgroups per launch (the MLP weights, same process: 2048 against
+// 4096 took the down sweep from 0.905 to 0.81 ms and the gate sweep from
+// 0.873 to 0.838 ms, half the per-workgroup set-up; 512 was 3% slower), and
+// the fewest rows per workgroup: two 64-row batches, so that a small weight's
+// workgroups amortise their set-up (the [2048, 2048] q_proj: 157 us in 512
+// workgroups of 128 rows against 162 us in 1024 of 64).
 constexpr int64_t kSweepWgs = 2048;
+constexpr int64_t kMinRowsPerWg = 128;
 // Rows of a workgroup's outputs that can be staged in LDS (8 batches of 64);
 // the launcher keeps rows_per_wg within it for any row count below 2^25.
 constexpr int kStageRows = 512;
@@ -521,7 +525,7 @@ inline dim3 sweep_grid(int64_t rows, int64_t k, int64_t* rows_per_wg) {
   const int64_t gx = (groups + kWaves - 1) / kWaves;
   int64_t rpw = (rows * gx + kSweepWgs - 1) / kSweepWgs;
   rpw = ((rpw + 63) / 64) * 64;
-  if (rpw < 64) rpw = 64;
+  if (rpw < kMinRowsPerWg) rpw = kMinRowsPerWg;
   if (rpw > kStageRows) rpw = kStageRows;                   // outputs staged in LDS (more workgroups instead)
   int64_t chunks = (rows + rpw - 1) / rpw;
   while (chunks > 65535) {
