@@ -20,6 +20,8 @@
 // Dequant ("NVFP4 量化流程说明" §5.4): DQ1 d = RN_f32(e4m3 * scale_2),
 // DQ2 RN_f32(e2m1 * d), cast to BF16 (v_cvt_pk_bf16_f32, nearest even); one
 // lane per half block.
+#include <type_traits>
+
 #include "common.hpp"
 #include "nvfp4_device.hpp"
 
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(256) void quantize_dynamic_kernel(const uint16_t* _
 // the first KiB (a) and of block 32 + l / 2 of the second (b); adjacent lanes
 // swap one half (DPP quad_perm 1,0,3,2), so that even lane 2j owns block j
 // and odd lane 2j + 1 owns block 32 + j, and from there each lane quantizes
-// its own block exactly as above.  Two units are in flight per wave.
+// its own block exactly as above.  A wave works on kPairUnits units per step
+// with the next two steps' loads in flight.
 constexpr int kPairUnits = 2;
 
 __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
@@ -284,61 +287,79 @@ __global__ __launch_bounds__(256) void quantize_units_kernel(const uint16_t* __r
   const bool odd = lane & 1;
   const int bi = odd ? 32 + (lane >> 1) : (lane >> 1);      // the block this lane owns after the swap
 
-  uint4 a[kPairUnits], b[kPairUnits];
-  auto load = [&](int64_t u) {
+  // two register sets, each holding kPairUnits units: the loop works on one
+  // while the other's loads are in flight, so two iterations of loads (and
+  // four units at the start, issued before the tables are built) are in
+  // flight per wave
+  uint4 a[2][kPairUnits], b[2][kPairUnits];
+  auto load = [&](int set, int64_t u) {
 #pragma unroll
     for (int q = 0; q < kPairUnits; ++q) {
       const int64_t uq = u + q * nwaves;
       if (uq < units) {
         const int64_t r = uq / upr;
         const uint4* src = reinterpret_cast<const uint4*>(x + r * ldx + (uq - r * upr) * 1024);
-        a[q] = ld_nt4(src + lane);
-        b[q] = ld_nt4(src + 64 + lane);
+        a[set][q] = ld_nt4(src + lane);
+        b[set][q] = ld_nt4(src + 64 + lane);
       }
     }
   };
-  load(u0);                                                  // before the tables: hides their set-up
+  const int64_t step = kPairUnits * nwaves;
+  load(0, u0);                                               // before the tables: hides their set-up
+  load(1, u0 + step);
   const float s2 = *scale2;
   const float inv = (float)(1.0 / (6.0 * (double)s2));
   const bool est = inv > 0.0f && inv < __builtin_inff();     // wave-uniform
   build_all_tables(tp, t, s2, force_exact);                     // syncs
-  const int mode = table_mode(t);
+  const int mode_rt = table_mode(t);
 
-  for (; u0 < units; u0 += kPairUnits * nwaves) {
-    uint32_t wv[kPairUnits][8];
+  // one copy of the loop per E2M1 mode (uniform over the launch), so the
+  // common modes run branch-free per block
+  auto run = [&](auto mode_c) {
+    constexpr int mode = decltype(mode_c)::value;
+    auto process = [&](int set, int64_t u) {
+      uint32_t wv[kPairUnits][8];
 #pragma unroll
-    for (int q = 0; q < kPairUnits; ++q) {
-      const uint4 send = odd ? a[q] : b[q];
-      const uint4 recv = make_uint4(swap_pair(send.x), swap_pair(send.y), swap_pair(send.z), swap_pair(send.w));
-      const uint4 lo = odd ? recv : a[q], hi = odd ? b[q] : recv;
-      wv[q][0] = lo.x; wv[q][1] = lo.y; wv[q][2] = lo.z; wv[q][3] = lo.w;
-      wv[q][4] = hi.x; wv[q][5] = hi.y; wv[q][6] = hi.z; wv[q][7] = hi.w;
-    }
-    load(u0 + kPairUnits * nwaves);                          // the next units in flight meanwhile
+      for (int q = 0; q < kPairUnits; ++q) {
+        const uint4 send = odd ? a[set][q] : b[set][q];
+        const uint4 recv = make_uint4(swap_pair(send.x), swap_pair(send.y), swap_pair(send.z), swap_pair(send.w));
+        const uint4 lo = odd ? recv : a[set][q], hi = odd ? b[set][q] : recv;
+        wv[q][0] = lo.x; wv[q][1] = lo.y; wv[q][2] = lo.z; wv[q][3] = lo.w;
+        wv[q][4] = hi.x; wv[q][5] = hi.y; wv[q][6] = hi.z; wv[q][7] = hi.w;
+      }
+      load(set, u + 2 * step);                               // this set's next units in flight meanwhile
 #pragma unroll
-    for (int q = 0; q < kPairUnits; ++q) {
-      const int64_t uq = u0 + q * nwaves;
-      if (uq < units) {
-        u16x2 m2 = u16x2{0, 0};
+      for (int q = 0; q < kPairUnits; ++q) {
+        const int64_t uq = u + q * nwaves;
+        if (uq < units) {
+          u16x2 m2 = u16x2{0, 0};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m2 = absmax2(m2, wv[q][i]);
-        const uint32_t P = max((uint32_t)m2.x, (uint32_t)m2.y);
-        const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
-        const uint2 qn = quantize_block(wv[q], c, t, mode);
-        const int64_t r = uq / upr;
-        const int64_t g = (uq - r * upr) * 64 + bi;          // block within the row
-        if constexpr (FQ) {
-          const float d = t.d[c];
-          uint4* dst = reinterpret_cast<uint4*>(out + r * ldo + g * 16);
-          dst[0] = dequant_word(qn.x, d);
-          dst[1] = dequant_word(qn.y, d);
-        } else {
-          st_nt2(packed + r * (k >> 1) + g * 8, qn);
-          st_nt1(codes + r * nb + g, (uint8_t)c);
+          for (int i = 0; i < 8; ++i) m2 = absmax2(m2, wv[q][i]);
+          const uint32_t P = max((uint32_t)m2.x, (uint32_t)m2.y);
+          const int c = est ? block_code_est(P, tp, inv) : block_code(P, tp, s2);
+          const uint2 qn = quantize_block(wv[q], c, t, mode);
+          const int64_t r = uq / upr;
+          const int64_t g = (uq - r * upr) * 64 + bi;        // block within the row
+          if constexpr (FQ) {
+            const float d = t.d[c];
+            uint4* dst = reinterpret_cast<uint4*>(out + r * ldo + g * 16);
+            dst[0] = dequant_word(qn.x, d);
+            dst[1] = dequant_word(qn.y, d);
+          } else {
+            st_nt2(packed + r * (k >> 1) + g * 8, qn);
+            st_nt1(codes + r * nb + g, (uint8_t)c);
+          }
         }
       }
+    };
+    for (; u0 < units; u0 += 2 * step) {
+      process(0, u0);
+      if (u0 + step < units) process(1, u0 + step);
     }
-  }
+  };
+  if (mode_rt == 0) run(std::integral_constant<int, 0>{});
+  else if (mode_rt == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 2>{});
 }
 
 static unsigned flat_grid(int64_t rows, int64_t nb, int64_t cap) {
@@ -346,11 +367,16 @@ static unsigned flat_grid(int64_t rows, int64_t nb, int64_t cap) {
   return (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
 }
 
-// grid of the unit kernel: about kQuantGrid workgroups, fewer for small inputs
+// grid of the unit kernel: about kUnitGrid workgroups, fewer for small inputs.
+// Three per CU: with two register sets of loads in flight the kernel takes
+// 146 VGPRs, so three waves fit per SIMD (measured on [8192, 4096], MALL
+// defeated: 19.1 us at 768 against 22.3 us at 1024 and 20.3 us at 512; the
+// one-set loop at 1024 took 19.5 us; bounding it to 128 VGPRs spilled).
+constexpr int kUnitGrid = 768;
 static unsigned unit_grid(int64_t rows, int64_t k) {
   const int64_t units = rows * ((k >> 4) >> 6);
   const int64_t want = (units + 4 * kPairUnits - 1) / (4 * kPairUnits);
-  return (unsigned)(want < kQuantGrid ? (want > 0 ? want : 1) : kQuantGrid);
+  return (unsigned)(want < kUnitGrid ? (want > 0 ? want : 1) : kUnitGrid);
 }
 
 int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
