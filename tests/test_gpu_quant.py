@@ -125,12 +125,13 @@ def test_quantize_random_scales(seed, path):
     _quant_case(x, s2)
 
 
-def test_dequant_all_codes():
-    note("dequant all codes")
+@pytest.mark.parametrize("k", [256, 2048])     # 2048: whole 64-block units (the unit kernel)
+def test_dequant_all_codes(k):
+    note(f"dequant all codes k={k}")
     rng = np.random.default_rng(9)
-    rows, k = 256, 256
+    rows = 256
     codes = rng.integers(0, 256, (rows, k // 16)).astype(np.uint8)
-    codes[0, :] = np.arange(16) + 0x70            # includes 0x7F (NaN)
+    codes[0, :16] = np.arange(16) + 0x70          # includes 0x7F (NaN)
     packed = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
     for s2 in (1.0, 3.7e-4, 2.0 ** -140):
         out = nq.dequant(to_dev_u8(packed), to_dev_u8(codes), to_dev_f32([s2]))
