@@ -154,18 +154,21 @@ __device__ __forceinline__ uint32_t fallback_requant(uint4 v, int delta, uint8_t
 // 32-64 bytes of loads in flight per thread (measured: with one run per step
 // the pass was latency-bound).  Other steps go block by block.  The code pair
 // of an E8M0 byte depends only on it and the group's k_max, so the workgroup
-// first tabulates all 256 bytes in LDS (kFallback marks a block outside the
-// window).  Codes go out with non-temporal stores (measured on MI355X: 139 ->
+// first tabulates all 256 bytes in LDS (entries of blocks outside the
+// window carry kFbFlag).  Codes go out with non-temporal stores (measured on MI355X: 139 ->
 // 115 us for the MoE expert set, MALL defeated; fewer workgroups were slower).
-// Fallback blocks are rare and scattered.  A step stores the usual fallback
-// code pair 0x0101 as a placeholder and appends the block to a list in LDS;
+// Fallback blocks are rare and scattered.  Their table entry is the usual
+// fallback code pair 0x0101, stored as a placeholder, with a flag in bit 31
+// (dropped when the pairs are packed); a lane whose run has a flagged entry
+// appends those blocks to a list in LDS;
 // after its last step the workgroup requantizes the whole list at once, each
 // thread taking one block with every nibble load issued before the first is
 // used (measured: per-lane handling inside the steps, even deferred by one
 // step, cost about 50 us of the pass on the MoE expert set).  Only a block
 // with an all-zero half needs its codes patched.  Blocks beyond the list's
 // capacity (not seen with realistic exponents) are handled at once.
-constexpr uint32_t kFallback = 0xFFFFu;
+constexpr uint32_t kFbFlag = 0x80000000u;
+constexpr uint32_t kFbEntry = kFbFlag | 0x0101u;
 constexpr int kFbCap = 2048;                            // fallback blocks listed per workgroup
 
 __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restrict__ packed,
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
     uint32_t t;
     if (b == 0xFF) t = 0x7F7Fu;
     else if (km - b <= 17) { const uint32_t c = pow2_code(8 - (km - b)); t = c | (c << 8); }
-    else t = kFallback;
+    else t = kFbEntry;
     tab[b] = t;
   }
   if (threadIdx.x == 0) fb_n = 0u;
@@ -231,25 +234,19 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
       for (int u = 0; u < kCodesSub; ++u) {
         const int64_t j = base + c0 + 8 * (threadIdx.x + kThreads * u);
         const uint32_t ew[2] = {cur[u].x, cur[u].y};
-        uint32_t c[4];
-        uint32_t fbmask = 0;
+        uint32_t cw[8];
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          uint32_t cw[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            cw[i] = tab[(ew[w] >> (8 * i)) & 0xFFu];
-            fbmask |= (cw[i] == kFallback ? 1u : 0u) << (4 * w + i);
-            cw[i] = cw[i] == kFallback ? 0x0101u : cw[i];
-          }
-          c[2 * w] = cw[0] | (cw[1] << 16);
-          c[2 * w + 1] = cw[2] | (cw[3] << 16);
-        }
-        st_nt4(codes + 2 * j, make_uint4(c[0], c[1], c[2], c[3]));
-        if (fbmask) {
+        for (int i = 0; i < 8; ++i) cw[i] = tab[(ew[i >> 2] >> (8 * (i & 3))) & 0xFFu];
+        // pairs of code pairs: low halves of two entries (drops the flag)
+        st_nt4(codes + 2 * j, make_uint4(__builtin_amdgcn_perm(cw[1], cw[0], 0x05040100u),
+                                         __builtin_amdgcn_perm(cw[3], cw[2], 0x05040100u),
+                                         __builtin_amdgcn_perm(cw[5], cw[4], 0x05040100u),
+                                         __builtin_amdgcn_perm(cw[7], cw[6], 0x05040100u)));
+        const uint32_t flags = cw[0] | cw[1] | cw[2] | cw[3] | cw[4] | cw[5] | cw[6] | cw[7];
+        if (flags & kFbFlag) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if ((fbmask >> i) & 1u) fallback_block_at(j + i, km - (int32_t)((ew[i >> 2] >> (8 * (i & 3))) & 0xFFu));
+            if (cw[i] & kFbFlag) fallback_block_at(j + i, km - (int32_t)((ew[i >> 2] >> (8 * (i & 3))) & 0xFFu));
         }
       }
     } else {
@@ -257,11 +254,8 @@ __global__ __launch_bounds__(kThreads) void cast_codes_kernel(uint8_t* __restric
       for (int64_t u = c0 + threadIdx.x; u < c1; u += kThreads) {
         const int64_t j = base + u;
         const uint32_t b = e8m0[j];
-        uint32_t cc = tab[b];
-        if (cc == kFallback) {
-          fallback_block_at(j, km - (int32_t)b);
-          cc = 0x0101u;
-        }
+        const uint32_t cc = tab[b];
+        if (cc & kFbFlag) fallback_block_at(j, km - (int32_t)b);
         codes[2 * j] = (uint8_t)(cc & 0xFFu);
         codes[2 * j + 1] = (uint8_t)(cc >> 8);
       }
