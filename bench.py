@@ -76,8 +76,6 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU baseline leg")
-    p.add_argument("--copy-probe", action="store_true",
-                   help="also run a 4 GiB torch elementwise copy (known bytes, for HBM counter scaling)")
     p.add_argument("--no-extras", action="store_true",
                    help="time the step only: skip the measured ceilings, the rotated-buffer stage timings, "
                         "the C2 leg and the pieces outside the step")
@@ -224,20 +222,20 @@ def main():
 
     def step(ev, b, wait_ev):
         """The timed step, on buffer set b (H, amax and scale_2 alternate
-        between consecutive steps).  The first HIP stream runs a1 and a4-a6,
-        then accumulates both calibration streams' H; the second takes the
-        gate/up sweeps once the first H is done and the down sweep once the
-        second is, every sweep capped at one workgroup per CU.  So the down
-        sweep of one step runs beside the next step's a1-a6 and first
-        Hessian; wait_ev (the second stream's end of the step two back, the
-        last reader of set b) guards the reuse of set b.  The HBM-bound
-        stages a1-a6 run in series with the HBM-bound accumulate rather than
-        beside it: measured on MI355X, beside it they slowed its calls by
-        about as much as their own time, for the same step time."""
+        between consecutive steps).  The first HIP stream runs a1, the
+        Hessians of both calibration streams, then a4-a6; the second takes
+        the gate/up sweeps once the first H is done and the down sweep once
+        the first stream's step is done, every sweep capped at one workgroup
+        per CU.  So the down sweep of one step runs beside the next step's a1
+        and first Hessian; wait_ev (the second stream's end of the step two
+        back, the last reader of set b) guards the reuse of set b.  The
+        HBM-bound stages run in series with the HBM-bound accumulate rather
+        than beside it (beside it they slowed its calls by about as much as
+        their own time), and a4-a6 run where the second stream is idle: next
+        to a capped sweep's 256-VGPR waves only one of their waves fits per
+        SIMD, which had made them 1.5-3.5x slower."""
         ev["start"].record(stream)
         stage_calls("a1_scale2", sptr, b)
-        for k in ("a4_quantize", "a5_dequant", "a6_restore", "a6_cast"):
-            stage_calls(k, sptr)
         if wait_ev is not None:
             stream.wait_event(wait_ev)
         for s in (0, 1):
@@ -249,6 +247,8 @@ def main():
         for n in ("gate", "up"):
             sweep(n, sptr_b, 1, b)
         hessian_stream(1, ev["h"], b)
+        for k in ("a4_quantize", "a5_dequant", "a6_restore", "a6_cast"):
+            stage_calls(k, sptr)
         ev["h1_done"].record(stream)
         side.wait_event(ev["h1_done"])
         sweep("down", sptr_b, 1, b)
@@ -570,23 +570,6 @@ def main():
         }
         del yq, wsq, xhq
 
-        if args.copy_probe:
-            # an elementwise kernel of known traffic (4 GiB read + 4 GiB written per
-            # launch): the reference for scaling the HBM byte counters
-            a = torch.zeros(1 << 31, dtype=torch.int16, device=dev)
-            b = torch.empty_like(a)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.neg(a, out=b)
-            e0.record(stream)
-            for _ in range(5):
-                torch.neg(a, out=b)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 5
-            stage_rep["hbm_copy_probe"] = {"kernel": "elementwise neg int16, 2^31 elements",
-                                           "bytes_read": a.numel() * 2, "bytes_written": a.numel() * 2,
-                                           "GBps": round(2 * a.numel() * 2 / (ms / 1e3) / 1e9, 1)}
-            del a, b
 
     value = blocks / (ms_per_step / 1e3)
     out = {
@@ -610,9 +593,9 @@ def main():
             "calibration_tokens": datagen.C4_TOKENS,
             "chunk_tokens": datagen.C4_CHUNK,
             "parallelism": "single GPU",
-            "schedule": "timed steps: a1, a4-a6 and then a2 of both calibration streams on one HIP stream; the "
+            "schedule": "timed steps: a1, a2 of both calibration streams, then a4-a6 on one HIP stream; the "
                         "three sweeps (capped at one workgroup per CU) on a second stream, the gate/up sweeps beside "
-                        "the second calibration stream's Hessian and the down sweep beside the next step's a1-a6 and "
+                        "the second calibration stream's Hessian and the down sweep beside the next step's a1 and "
                         "first Hessian (two alternating sets of H/amax/scale_2 buffers; checked bit-exact against "
                         "the serial order); stages: the same work in stage order on one stream",
             "serial_step_ms": round(step_ms, 4),
