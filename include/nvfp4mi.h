@@ -96,6 +96,29 @@ int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out,
                          float* amax_out, void* stream);
 
 /*
+ * Step 1 for several tensors at once (a Linear's weight and its calibration
+ * activations, the weights of one MLP, ...): for t < count, exactly what
+ * nvfp4_compute_scale2(xs[t], ns[t], scale2_out + t, amax_out + t) gives,
+ * in three kernel launches in all instead of three per tensor (the reduce
+ * walks the tensors in turn, one atomic max per workgroup and tensor).
+ *
+ * xs, ns     HOST arrays of count entries: device pointers to bf16 tensors
+ *            (contiguous, 16-byte aligned; NULL allowed where ns[t] == 0) and
+ *            their element counts.  Read during the call only.
+ * count      1 .. 16.
+ * scale2_out device float[count]: receives the scale_2 values; also the
+ *            running accumulators when amax_out is NULL, so it must not
+ *            alias any input.
+ * amax_out   device float[count] or NULL: receives the amax values (and is
+ *            then the accumulator).
+ * Errors: BAD_SHAPE (count out of range, ns[t] < 0), NULL_ARG (xs, ns,
+ *         scale2_out, or xs[t] with ns[t] > 0), MISALIGNED (xs[t]; the
+ *         output arrays not 4-byte aligned), HIP.
+ */
+int nvfp4_compute_scale2_batch(const uint16_t* const* xs, const int64_t* ns, int count,
+                               float* scale2_out, float* amax_out, void* stream);
+
+/*
  * Bytes of workspace nvfp4_hessian_accum and nvfp4_hessian_accum_fq need for
  * (tokens, k) (one size serves both); 0 when tokens == 0.  Returns 0 for
  * invalid sizes too (the accumulate call then reports the shape error).

@@ -21,7 +21,7 @@ import os
 import torch
 
 __all__ = [
-    "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "hessian_workspace_bytes",
+    "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "compute_scale2_batch", "hessian_workspace_bytes",
     "hessian_accum", "hessian_accum_noalloc", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
     "fp8_compute_scale", "fp8_quantize", "fp8_dequant", "block_hadamard", "hessian_hadamard",
     "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward", "scale_sweep_stats",
@@ -36,6 +36,8 @@ _i64 = ctypes.c_int64
 _SIGS = {
     "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4_compute_scale2": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "nvfp4_compute_scale2_batch": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(_i64), ctypes.c_int,
+                                                  _c_void_p, _c_void_p, _c_void_p]),
     "nvfp4_hessian_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_hessian_accum": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                            ctypes.c_size_t, _c_void_p]),
@@ -137,6 +139,36 @@ def compute_scale2(x: torch.Tensor, out=None):
         _dev(am, torch.float32, "amax")
     _check("nvfp4_compute_scale2",
            load().nvfp4_compute_scale2(x.data_ptr(), x.numel(), s2.data_ptr(), am.data_ptr(), _stream(x)))
+    return s2, am
+
+
+def compute_scale2_batch(xs, out=None):
+    """compute_scale2 for up to 16 contiguous bf16 tensors in one call (three
+    launches in all).  Returns (scale2, amax), each f32[len(xs)], on the first
+    tensor's device and stream; out=(scale2, amax) reuses buffers."""
+    xs = list(xs)
+    if not xs or len(xs) > 16:
+        raise ValueError("compute_scale2_batch takes 1 to 16 tensors")
+    for i, x in enumerate(xs):
+        _dev(x, torch.bfloat16, f"xs[{i}]")
+        if not x.is_contiguous():
+            raise ValueError(f"xs[{i}] must be contiguous")
+        if x.device != xs[0].device:
+            raise ValueError("all tensors must be on one device")
+    n = len(xs)
+    if out is None:
+        s2 = torch.empty(n, dtype=torch.float32, device=xs[0].device)
+        am = torch.empty(n, dtype=torch.float32, device=xs[0].device)
+    else:
+        s2, am = out
+        _dev(s2, torch.float32, "scale2")
+        _dev(am, torch.float32, "amax")
+        if s2.numel() < n or am.numel() < n:
+            raise ValueError("out buffers too small")
+    ptrs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    counts = (_i64 * n)(*[x.numel() for x in xs])
+    _check("nvfp4_compute_scale2_batch", load().nvfp4_compute_scale2_batch(
+        ptrs, counts, n, s2.data_ptr(), am.data_ptr(), _stream(xs[0])))
     return s2, am
 
 

@@ -73,6 +73,19 @@ int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float*
   return launch_compute_scale2(x, n, scale2_out, amax_out, as_stream(stream));
 }
 
+int nvfp4_compute_scale2_batch(const uint16_t* const* xs, const int64_t* ns, int count, float* scale2_out,
+                               float* amax_out, void* stream) {
+  if (count < 1 || count > kScaleBatch) return NVFP4_ERR_BAD_SHAPE;
+  if (!xs || !ns || !scale2_out) return NVFP4_ERR_NULL_ARG;
+  for (int t = 0; t < count; ++t) {
+    if (ns[t] < 0 || !mul_fits(ns[t], 2)) return NVFP4_ERR_BAD_SHAPE;
+    if (ns[t] > 0 && !xs[t]) return NVFP4_ERR_NULL_ARG;
+    if (ns[t] > 0 && !aligned16(xs[t])) return NVFP4_ERR_MISALIGNED;
+  }
+  if (!aligned4(scale2_out) || (amax_out && !aligned4(amax_out))) return NVFP4_ERR_MISALIGNED;
+  return launch_compute_scale2_batch(xs, ns, count, scale2_out, amax_out, as_stream(stream));
+}
+
 size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k) {
   if (tokens <= 0 || k <= 0 || (k % 16) != 0) return 0;
   return hessian_workspace_bytes(tokens, k);

@@ -34,6 +34,9 @@ int force_exact_flag();
 
 // Launchers (one per kernel family); arguments are validated by the caller.
 int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, hipStream_t s);
+constexpr int kScaleBatch = 16;          // tensors per nvfp4_compute_scale2_batch call
+int launch_compute_scale2_batch(const uint16_t* const* xs, const int64_t* ns, int count, float* scale2_out,
+                                float* amax_out, hipStream_t s);
 int launch_quantize_dynamic(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, const float* scale2,
                             uint8_t* packed, uint8_t* codes, hipStream_t s);
 int launch_dequant(const uint8_t* packed, const uint8_t* codes, const float* scale2, int64_t rows, int64_t k,

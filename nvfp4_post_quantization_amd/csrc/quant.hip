@@ -33,8 +33,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- amax ----
 
-__global__ void amax_init_kernel(uint32_t* acc) {
-  if (threadIdx.x == 0) *acc = 0u;
+// Up to kScaleBatch tensors per launch: workgroup w takes its grid-stride
+// share of tensor 0, then of tensor 1, ..., so no workgroup idles at a
+// tensor boundary; one atomicMax per workgroup and tensor.  acc[t] is
+// amax_out[t] when given, else scale2_out[t] (both FP32 arrays of count).
+struct AmaxBatch {
+  const uint16_t* x[kScaleBatch];
+  int64_t n[kScaleBatch];
+  uint32_t* acc[kScaleBatch];
+  float* scale_out[kScaleBatch];
+  float* amax_out[kScaleBatch];
+  int count;
+  int fp8;
+};
+
+__global__ void amax_init_kernel(const AmaxBatch b) {
+  if ((int)threadIdx.x < b.count) *b.acc[threadIdx.x] = 0u;
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
@@ -49,6 +63,7 @@ __device__ __forceinline__ void publish_max(uint32_t m, uint32_t* acc) {
   __shared__ uint32_t part[8];
   m = wave_max(m);
   int w = threadIdx.x >> 6;
+  __syncthreads();                       // the previous tensor's reads of part are done
   if ((threadIdx.x & 63) == 0) part[w] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -56,11 +71,6 @@ __device__ __forceinline__ void publish_max(uint32_t m, uint32_t* acc) {
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = max(r, part[i]);
     if (r) atomicMax(acc, r << 16);
   }
-}
-
-__device__ __forceinline__ uint32_t absmax_word(uint32_t m, uint32_t v) {
-  m = max(m, v & 0x7FFFu);
-  return max(m, (v >> 16) & 0x7FFFu);
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -73,67 +83,86 @@ __device__ __forceinline__ u16x2 absmax2(u16x2 m, uint32_t v) {
 constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per thread
 constexpr int kAmaxGrid = 256;          // one workgroup per CU: fewest same-address atomics (measured best)
 
-__global__ __launch_bounds__(256) void amax_reduce_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                          uint32_t* acc) {
-  const uint4* x16 = reinterpret_cast<const uint4*>(x);
-  const int64_t n16 = n >> 3;
+__global__ __launch_bounds__(256) void amax_reduce_kernel(const AmaxBatch b) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  u16x2 m2 = u16x2{0, 0};
-  int64_t i = gid;
-  for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
-    uint4 v[kAmaxUnroll];
+  for (int t = 0; t < b.count; ++t) {
+    const uint16_t* __restrict__ x = b.x[t];
+    const int64_t n = b.n[t];
+    const uint4* x16 = reinterpret_cast<const uint4*>(x);
+    const int64_t n16 = n >> 3;
+    u16x2 m2 = u16x2{0, 0};
+    int64_t i = gid;
+    for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
+      uint4 v[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = ld_nt4(x16 + i + u * stride);
+      for (int u = 0; u < kAmaxUnroll; ++u) v[u] = ld_nt4(x16 + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) {
-      m2 = absmax2(m2, v[u].x); m2 = absmax2(m2, v[u].y); m2 = absmax2(m2, v[u].z); m2 = absmax2(m2, v[u].w);
+      for (int u = 0; u < kAmaxUnroll; ++u) {
+        m2 = absmax2(m2, v[u].x); m2 = absmax2(m2, v[u].y); m2 = absmax2(m2, v[u].z); m2 = absmax2(m2, v[u].w);
+      }
     }
+    for (; i < n16; i += stride) {
+      const uint4 v = x16[i];
+      m2 = absmax2(m2, v.x); m2 = absmax2(m2, v.y); m2 = absmax2(m2, v.z); m2 = absmax2(m2, v.w);
+    }
+    uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
+    if (gid < n - (n16 << 3)) m = max(m, (uint32_t)x[(n16 << 3) + gid] & 0x7FFFu);
+    publish_max(m, b.acc[t]);
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = x16[i];
-    m2 = absmax2(m2, v.x); m2 = absmax2(m2, v.y); m2 = absmax2(m2, v.z); m2 = absmax2(m2, v.w);
-  }
-  uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
-  if (gid < n - (n16 << 3)) m = max(m, (uint32_t)x[(n16 << 3) + gid] & 0x7FFFu);
-  publish_max(m, acc);
 }
 
 // scale = amax / 6 / 448 (NVFP4 tensor scale) or amax / 448 (FP8 E4M3
 // per-tensor scale), in double and then stored as FP32.
-__global__ void amax_finalize_kernel(const uint32_t* acc, float* scale2_out, float* amax_out, int fp8) {
-  if (threadIdx.x == 0) {
-    float amax = __uint_as_float(*acc);
-    float s2 = fp8 ? (float)((double)amax / 448.0) : (float)((double)amax / 6.0 / 448.0);
-    if (amax_out) *amax_out = amax;
-    *scale2_out = s2;
+__global__ void amax_finalize_kernel(const AmaxBatch b) {
+  const int t = threadIdx.x;
+  if (t < b.count) {
+    float amax = __uint_as_float(*b.acc[t]);
+    float s2 = b.fp8 ? (float)((double)amax / 448.0) : (float)((double)amax / 6.0 / 448.0);
+    if (b.amax_out[t]) *b.amax_out[t] = amax;
+    *b.scale_out[t] = s2;
   }
 }
 
-static int launch_amax_scale(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, int fp8,
-                             hipStream_t s) {
-  uint32_t* acc = reinterpret_cast<uint32_t*>(amax_out ? amax_out : scale2_out);
-  amax_init_kernel<<<1, 64, 0, s>>>(acc);
+static int launch_amax_batch(const uint16_t* const* xs, const int64_t* ns, int count, float* scale_out,
+                             float* amax_out, int fp8, hipStream_t s) {
+  AmaxBatch b{};
+  b.count = count;
+  b.fp8 = fp8;
+  int64_t most = 0;
+  for (int t = 0; t < count; ++t) {
+    b.x[t] = xs[t];
+    b.n[t] = ns[t];
+    b.scale_out[t] = scale_out + t;
+    b.amax_out[t] = amax_out ? amax_out + t : nullptr;
+    b.acc[t] = reinterpret_cast<uint32_t*>(amax_out ? amax_out + t : scale_out + t);
+    if (ns[t] > most) most = ns[t];
+  }
+  amax_init_kernel<<<1, 64, 0, s>>>(b);
   int st = launch_status("amax_init_kernel");
   if (st) return st;
-  if (n > 0) {
-    int64_t n16 = n >> 3;
-    int64_t want = (n16 + 256 * kAmaxUnroll - 1) / (256 * kAmaxUnroll);
-    int grid = (int)(want < kAmaxGrid ? (want > 0 ? want : 1) : kAmaxGrid);
-    amax_reduce_kernel<<<grid, 256, 0, s>>>(x, n, acc);
+  if (most > 0) {
+    const int64_t want = ((most >> 3) + 256 * kAmaxUnroll - 1) / (256 * kAmaxUnroll);
+    const int grid = (int)(want < kAmaxGrid ? (want > 0 ? want : 1) : kAmaxGrid);
+    amax_reduce_kernel<<<grid, 256, 0, s>>>(b);
     st = launch_status("amax_reduce_kernel");
     if (st) return st;
   }
-  amax_finalize_kernel<<<1, 64, 0, s>>>(acc, scale2_out, amax_out, fp8);
+  amax_finalize_kernel<<<1, 64, 0, s>>>(b);
   return launch_status("amax_finalize_kernel");
 }
 
 int launch_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float* amax_out, hipStream_t s) {
-  return launch_amax_scale(x, n, scale2_out, amax_out, 0, s);
+  return launch_amax_batch(&x, &n, 1, scale2_out, amax_out, 0, s);
+}
+
+int launch_compute_scale2_batch(const uint16_t* const* xs, const int64_t* ns, int count, float* scale2_out,
+                                float* amax_out, hipStream_t s) {
+  return launch_amax_batch(xs, ns, count, scale2_out, amax_out, 0, s);
 }
 
 int launch_fp8_scale(const uint16_t* x, int64_t n, float* scale_out, float* amax_out, hipStream_t s) {
-  return launch_amax_scale(x, n, scale_out, amax_out, 1, s);
+  return launch_amax_batch(&x, &n, 1, scale_out, amax_out, 1, s);
 }
 
 // ------------------------------------------------------ dynamic quantizer ----

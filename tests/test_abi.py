@@ -38,7 +38,7 @@ def lib():
 def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) == {
-        "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_hessian_workspace_bytes",
+        "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_compute_scale2_batch", "nvfp4_hessian_workspace_bytes",
         "nvfp4_hessian_accum", "nvfp4_hessian_accum_noalloc", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
         "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant", "nvfp4_scale_sweep_ex",
@@ -66,6 +66,26 @@ def test_compute_scale2_validation(lib):
     assert lib.nvfp4_compute_scale2(None, 16, P, None, None) == NULL
     assert lib.nvfp4_compute_scale2(P, 16, None, None, None) == NULL
     assert lib.nvfp4_compute_scale2(P + 2, 16, P, None, None) == ALIGN
+
+
+def test_compute_scale2_batch_validation(lib):
+    f = lib.nvfp4_compute_scale2_batch
+    def arrs(ptrs, ns):
+        return (ctypes.c_void_p * len(ptrs))(*ptrs), (ctypes.c_int64 * len(ns))(*ns)
+    xs, ns = arrs([P, P + 16], [16, 32])
+    assert f(xs, ns, 0, P, None, None) == SHAPE                           # count < 1
+    assert f(xs, ns, 17, P, None, None) == SHAPE                          # count > 16
+    assert f(None, ns, 2, P, None, None) == NULL
+    assert f(xs, None, 2, P, None, None) == NULL
+    assert f(xs, ns, 2, None, None, None) == NULL
+    xs2, ns2 = arrs([P, None], [16, 8])
+    assert f(xs2, ns2, 2, P, None, None) == NULL                          # null tensor with n > 0
+    xs3, ns3 = arrs([P, P + 2], [16, 8])
+    assert f(xs3, ns3, 2, P, None, None) == ALIGN                         # tensor not 16-byte aligned
+    xs4, ns4 = arrs([P, P], [16, -1])
+    assert f(xs4, ns4, 2, P, None, None) == SHAPE                         # n < 0
+    assert f(xs, ns, 2, P + 2, None, None) == ALIGN                       # scale2_out not 4-byte aligned
+    assert f(xs, ns, 2, P, P + 1, None) == ALIGN                          # amax_out
 
 
 def test_hessian_validation(lib):

@@ -62,6 +62,38 @@ def test_scale2_configs():
         _check_scale2(b)
 
 
+def test_scale2_batch_matches_single_calls():
+    """The batched step 1 over tensors of mixed sizes (empty, a ragged tail,
+    a repeated tensor, 16 at once) gives each tensor's amax and scale_2
+    exactly as the single-tensor call and the oracle do; with amax_out NULL
+    the scale_2 array doubles as the accumulator."""
+    import ctypes
+    note("compute_scale2_batch")
+    rng = np.random.default_rng(17)
+    sizes = [0, 7, 8, 4095, 1 << 16, 3 * (1 << 20) + 5, 16, 1, 96, 1 << 12, 17, 33, 64, 1000, 2048, 5]
+    hosts = [datagen.f32_to_bf16_bits((rng.laplace(0, 1, n) * np.exp(rng.uniform(-20, 20))).astype(np.float32))
+             for n in sizes]
+    devs = [to_dev_bf16(h) if h.size else torch.empty(0, dtype=torch.bfloat16, device=DEV) for h in hosts]
+    devs[8], hosts[8] = devs[5], hosts[5]               # the same tensor twice
+    devs[9] = devs[4][: sizes[9]]                       # a view into another tensor of the batch
+    hosts[9] = hosts[4][: sizes[9]]
+    s2, am = nq.compute_scale2_batch(devs)
+    for t, h in enumerate(hosts):
+        ref_am, ref_s2 = N.tensor_scale(h)
+        assert float(host(am)[t]) == ref_am and float(host(s2)[t]) == float(np.float32(ref_s2)), t
+        if h.size:
+            s1, a1 = nq.compute_scale2(devs[t])
+            assert float(host(s1)[0]) == float(host(s2)[t]) and float(host(a1)[0]) == float(host(am)[t])
+    for count in (1, 3):                                # amax_out NULL: scale2_out accumulates
+        lib = nq.load()
+        ptrs = (ctypes.c_void_p * count)(*[d.data_ptr() for d in devs[4:4 + count]])
+        ns = (ctypes.c_int64 * count)(*[d.numel() for d in devs[4:4 + count]])
+        out = torch.full((count,), 7.0, dtype=torch.float32, device=DEV)   # stale contents
+        assert lib.nvfp4_compute_scale2_batch(ptrs, ns, count, out.data_ptr(), None,
+                                              torch.cuda.current_stream().cuda_stream) == 0
+        assert torch.equal(out, s2[4:4 + count])
+
+
 def _quant_case(bits2d: np.ndarray, s2: float, ld: int | None = None):
     rows, k = bits2d.shape
     if ld is None:
