@@ -685,13 +685,14 @@ def sweep_work(lib, chk, w, H, s2, ref_out, sptr):
     return [int(v) for v in st.cpu().tolist()]
 
 
-# the sources each profiled kernel is built from; a committed counter line
-# applies while their hashes (first 16 hex digits of sha256, joined by "+")
-# match the ones it was taken on
+# the sources each profiled kernel's device code comes from (common.hpp holds
+# host-side declarations only); a committed counter line applies while their
+# hashes (first 16 hex digits of sha256, joined by "+") match the ones it was
+# taken on
 KERNEL_SOURCES = {
-    "sweep_kernel": ("sweep_kernel.hpp", "sweep.hip", "nvfp4_device.hpp", "common.hpp"),
-    "hessian_partial_kernel": ("hessian.hip", "nvfp4_device.hpp", "common.hpp"),
-    "hessian_reduce_kernel": ("hessian.hip", "nvfp4_device.hpp", "common.hpp"),
+    "sweep_kernel": ("sweep_kernel.hpp", "sweep.hip", "nvfp4_device.hpp"),
+    "hessian_partial_kernel": ("hessian.hip", "nvfp4_device.hpp"),
+    "hessian_reduce_kernel": ("hessian.hip", "nvfp4_device.hpp"),
 }
 
 
