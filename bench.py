@@ -5,7 +5,8 @@ One step is one pass of every stage of the path over resident synthetic
 inputs:
   * the hybrid-model MLP set (gate/up W [12288, 4096], down W [4096, 12288];
     2^20 calibration tokens streamed as 16 chunks of 65536 per Linear input):
-      a1 tensor amax -> scale_2 of each weight,
+      a1 tensor amax -> scale_2 of each weight (one batched call with the
+         activations' a1 below),
       a2 block-diagonal Hessian of both input streams (32 chunk calls, the
          activation amax fused into the same read),
       a3 the Hessian-weighted E4M3 scale sweep of all three weights
@@ -15,7 +16,7 @@ inputs:
   * 128 MoE experts x (w1, w3) [2048, 7168] MXFP4: a6 the MXFP4->NVFP4 cast
     (in place on the nibbles, so each step first restores the original
     nibbles of the fallback blocks, ~9 MB, inside the timed step).
-After the timed steps, two neighbouring pieces are timed on their own and
+After the timed steps, the neighbouring pieces are timed on their own and
 reported under stages (not part of the step): the W4A4 form of a2 (Hessian
 of the fake-quantized calibration streams, next_w4a4_hessian), the FP8 E4M3
 per-tensor static tier on the C3 activations (next_fp8_static), the
@@ -25,13 +26,13 @@ of one calibration chunk through the swept gate weight
 (next_quantlinear_forward).
 
 The headline value is weight blocks swept per second of whole-step time.
-In the timed steps one HIP stream accumulates the Hessians and a second runs
-everything else: a1 and a4-a6, the gate/up sweeps once the first
-calibration stream's H is done (beside the second stream's Hessian), and
-the down sweep once the second H is done (beside the next step's first
-Hessian: consecutive steps alternate between two sets of H, amax and
-scale_2 buffers).  Every sweep there is capped at one workgroup per CU so
-that the Hessian keeps its own workgroups resident beside it.  Both buffer
+In the timed steps one HIP stream runs a1, the Hessians and then a4-a6, and
+a second runs the sweeps: gate/up once the first calibration stream's H is
+done (beside the second stream's Hessian), down once the first stream's
+step is done (beside the next step's a1 and first Hessian: consecutive
+steps alternate between two sets of H, amax and scale_2 buffers).  Every
+sweep there is capped at one workgroup per CU so that the Hessian keeps its
+own workgroups resident beside it.  Both buffer
 sets must hold identical results, and one serial step afterwards must
 reproduce every output bit for bit.  Per-stage times come from HIP events
 over the same work in stage order on one stream.
