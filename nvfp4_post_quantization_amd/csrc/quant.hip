@@ -1,4 +1,5 @@
-// Tensor amax -> scale_2, the dynamic per-16 NVFP4 quantizer, and the
+// Tensor amax -> scale_2 (one tensor, or up to kScaleBatch tensors in the
+// same three launches), the dynamic per-16 NVFP4 quantizer, and the
 // two-DequantizeLinear chain.  All three are single HBM passes.
 //
 // scale_2 = amax / (6 * 448) ("NVFP4 量化流程说明" §3.4), computed as the
@@ -8,7 +9,8 @@
 //
 // Dynamic quantizer ("NVFP4 量化流程说明" §3.4-§3.5): one lane per 16-element
 // block (for rows of whole 64-block units, the blocks reach their lanes
-// through contiguous 1 KiB wave loads and one DPP exchange of half blocks).  The block code RNE(amax_b / (6 scale_2)) is estimated from the FP32
+// through contiguous 1 KiB wave loads and one DPP exchange of half blocks).
+// The block code RNE(amax_b / (6 scale_2)) is estimated from the FP32
 // quotient and made exact against 126 bf16-pattern thresholds (one per E4M3
 // midpoint; binary search when 1/(6 scale_2) overflows);
 // the elements are then quantized with the certified fast path or the exact
@@ -19,7 +21,8 @@
 //
 // Dequant ("NVFP4 量化流程说明" §5.4): DQ1 d = RN_f32(e4m3 * scale_2),
 // DQ2 RN_f32(e2m1 * d), cast to BF16 (v_cvt_pk_bf16_f32, nearest even); one
-// lane per half block.
+// lane per block of a 64-block unit for rows of whole units, else one lane
+// per half block.
 #include <type_traits>
 
 #include "common.hpp"
@@ -178,7 +181,7 @@ __device__ __forceinline__ uint2 quantize_block(const uint32_t* wv, int c, const
 constexpr int kUnits = 4;                // blocks per thread per batch (loads in flight)
 constexpr int kQuantGrid = 1024;         // quantizers: four workgroups per CU hide the E2M1 work (measured
                                          // 23.6 -> 21.0 us on [8192, 4096] against 512)
-constexpr int kDequantGrid = 512;        // dequant: two per CU (1024 measured 9% slower)
+constexpr int kDequantGrid = 512;        // half-block dequant: two per CU (1024 measured 9% slower)
 
 // Position of flat block index u (row-major [rows][nb]) advanced by a fixed
 // stride without a 64-bit division per step.
