@@ -7,8 +7,9 @@ inputs:
     2^20 calibration tokens streamed as 16 chunks of 65536 per Linear input):
       a1 tensor amax -> scale_2 of each weight (one batched call with the
          activations' a1 below),
-      a2 block-diagonal Hessian of both input streams (32 chunk calls, the
-         activation amax fused into the same read),
+      a2 block-diagonal Hessian of both input streams (one call per stream
+         over its 16 resident chunks, the activation amax fused into the same
+         read),
       a3 the Hessian-weighted E4M3 scale sweep of all three weights
          (9,437,184 blocks);
   * activations X [8192, 4096]: a1 amax, a4 dynamic NVFP4 quantization and
@@ -145,6 +146,10 @@ def main():
     H, amax_x = Hb[0], amax_xb[0]
     ws_bytes = max(nq.hessian_workspace_bytes(datagen.C4_CHUNK, k) for k in (4096, 12288))
     ws = torch.empty(ws_bytes, **u8)
+    # the chunk-list accumulate: one call per calibration stream over its 16 chunks
+    wsc_bytes = max(nq.hessian_chunks_workspace_bytes(datagen.C4_CHUNK, k, 16) for k in (4096, 12288))
+    wsc = torch.empty(wsc_bytes, **u8)
+    x_ptrs = [(ctypes.c_void_p * len(X[s]))(*[x.data_ptr() for x in X[s]]) for s in (0, 1)]
     # step 1 of the three weights and the C3 activations in one batched call:
     # per buffer set, scale_2 and amax of [gate, up, down, X] in one array each
     s2_all = [torch.zeros(4, **f32) for _ in range(NB)]
@@ -201,13 +206,14 @@ def main():
                                               c.data_ptr(), None, wgs_per_cu, sp))
 
     def hessian_stream(s, evh, b=0):
-        """The 16 chunk calls of calibration stream s, bracketed by one event
-        pair (an event between calls would leave the GPU idle ~10 us each)."""
+        """Calibration stream s's Hessian: one chunk-list call over its 16
+        resident chunks (one accumulate pass and one reduce), bracketed by an
+        event pair on its stream."""
         evh[s][0].record(stream)
-        for x in X[s]:
-            chk("hessian", lib.nvfp4_hessian_accum(x.data_ptr(), x.shape[0], x.shape[1], x.shape[1],
-                                                   Hb[b][s].data_ptr(), amax_xb[b][s].data_ptr(), ws.data_ptr(),
-                                                   ws.numel(), sptr))
+        x0 = X[s][0]
+        chk("hessian", lib.nvfp4_hessian_accum_chunks(x_ptrs[s], len(X[s]), x0.shape[0], x0.shape[1], x0.shape[1],
+                                                      Hb[b][s].data_ptr(), amax_xb[b][s].data_ptr(), wsc.data_ptr(),
+                                                      wsc.numel(), sptr))
         evh[s][1].record(stream)
 
     def step_serial(ev):
@@ -286,7 +292,7 @@ def main():
     wall = time.perf_counter() - t_begin
     ms_per_step = wall * 1e3 / args.steps
     # mean Hessian call (partial + reduce) on its stream inside the timed steps
-    h_call_ms = sum(a.elapsed_time(b) for ev in evs for a, b in ev["h"]) / (args.steps * 32)
+    h_call_ms = sum(a.elapsed_time(b) for ev in evs for a, b in ev["h"]) / (args.steps * 2)
 
     # the overlapped schedule must produce exactly what the serial order does
     def outputs(b=0):
@@ -326,7 +332,7 @@ def main():
             st_ms[k] += prev.elapsed_time(ev[k]) / n_serial
             prev = ev[k]
         step_ms += ev["start"].elapsed_time(ev["a6_cast"]) / n_serial
-    h_call_serial_ms = sum(a.elapsed_time(b) for ev in evs_serial for a, b in ev["h"]) / (n_serial * 32)
+    h_call_serial_ms = sum(a.elapsed_time(b) for ev in evs_serial for a, b in ev["h"]) / (n_serial * 2)
 
     # algorithmic work per step
     blocks = sum(w.numel() // 16 for w in W.values())
@@ -336,7 +342,7 @@ def main():
     cast_bytes = E5.numel() + c5[0].numel() + fb * C5_FALLBACK_BYTES     # the restore of the inputs not counted
     info = {
         "a1_scale2": dict(launches=1, bytes=a1_bytes),
-        "a2_hessian": dict(launches=32, bytes=x_bytes),
+        "a2_hessian": dict(launches=2, bytes=x_bytes),
         "a3_sweep": dict(launches=3, blocks=blocks),
         "a4_quantize": dict(launches=1, bytes=q_bytes),
         "a5_dequant": dict(launches=1, bytes=q_bytes),
@@ -379,12 +385,13 @@ def main():
                               f"{st_ms[dom] / 3:.4f} ms avg"}
     else:
         per_launch_s = h_call_ms / 1e3                               # live, on its stream, in the timed steps
-        achieved = x_bytes / 32 / per_launch_s / 1e9
-        alone = x_bytes / 32 / (h_call_serial_ms / 1e3) / 1e9
+        achieved = x_bytes / 2 / per_launch_s / 1e9
+        alone = x_bytes / 2 / (h_call_serial_ms / 1e3) / 1e9
         roof = {"kernel": "hessian_partial_kernel+hessian_reduce_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "per_launch": f"{x_bytes / 32 / 1e9:.4f} GB avg, {per_launch_s * 1e3:.4f} ms avg (events around "
-                              f"each calibration stream's 16 calls, on their stream, in the timed steps, where they "
+                "per_launch": f"{x_bytes / 2 / 1e9:.4f} GB avg, {per_launch_s * 1e3:.4f} ms avg (one "
+                              f"nvfp4_hessian_accum_chunks call per calibration stream over its 16 chunks: events "
+                              f"around each call, on its stream, in the timed steps, where they "
                               f"share the GPU with the second stream's sweeps)",
                 "alone": {"ms_per_launch": round(h_call_serial_ms, 4), "achieved": round(alone, 1),
                           "frac": round(alone / HBM_PEAK_GBS, 4),
@@ -860,7 +867,8 @@ def c2_leg(lib, chk, dev, stream, sptr, ceil, reps=20):
 
 def traffic_from_profiles(kernel: str):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy
-    probe) from the committed counter summary; null unless every kernel of
+    probe) from the committed counter summary, times each kernel's launches
+    per call where the summary states them; null unless every kernel of
     `kernel` ("a+b" sums them) was measured on its current source."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     total = 0.0
@@ -872,7 +880,7 @@ def traffic_from_profiles(kernel: str):
             hit = [f for f in lines if f.get("kernel") == name and f.get("src_sha") == sha]
             if not hit:
                 return None
-            total += float(hit[0]["hbm_bytes_per_launch"])
+            total += float(hit[0]["hbm_bytes_per_launch"]) * float(hit[0].get("launches_per_call", 1))
     except (OSError, KeyError, ValueError):
         return None
     return round(total, 1)

@@ -150,6 +150,34 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Step 2 over several resident chunks of one calibration stream in one call
+ * (for callers that keep a stream's activations in device memory): for every
+ * group g,  H[g] += sum over chunks c of X_c[:, 16g:16g+16]^T X_c[:, 16g:16g+16].
+ * One accumulate pass over all chunks and one reduce, instead of a pass and a
+ * reduce per chunk.  The fp32 partial sums are exactly those of one
+ * nvfp4_hessian_accum call per chunk; they are then added in fp64 (chunk by
+ * chunk, each in workgroup order) and H is rounded once, so the result may
+ * differ from nvfp4_hessian_accum chunk by chunk in the last bits of H (it
+ * rounds H once instead of once per chunk) and is bitwise reproducible.
+ *
+ * xs         HOST array of nchunks device pointers, each [tokens][ldx] bf16
+ *            (columns 0..k-1 used; 16-byte aligned rows).  Read during the call.
+ * nchunks    1 .. 64.
+ * tokens, k, ldx, H, amax_inout, stream: as for nvfp4_hessian_accum (every
+ *            chunk has the same shape; amax_inout is raised to the max |x|
+ *            over all chunks).
+ * workspace  16-byte aligned device buffer of at least
+ *            nvfp4_hessian_chunks_workspace_bytes(tokens, k, nchunks) bytes
+ *            (one chunk's plain-kernel partial slots per chunk); scratch.
+ * Errors: as for nvfp4_hessian_accum, plus BAD_SHAPE for nchunks out of range
+ *         and NULL_ARG for xs or a NULL chunk.
+ */
+size_t nvfp4_hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchunks);
+int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens,
+                               int64_t k, int64_t ldx, float* H, float* amax_inout,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_hessian_accum without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same operation, kernels and results (bit for bit)

@@ -114,6 +114,32 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
   return launch_hessian_accum(x, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
 }
 
+size_t nvfp4_hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchunks) {
+  if (tokens <= 0 || k <= 0 || (k % 16) != 0 || nchunks < 1 || nchunks > kMaxChunks) return 0;
+  if (!mul_fits(tokens, k) || !mul_fits(tokens * k, 2)) return 0;
+  return hessian_chunks_workspace_bytes(tokens, k, nchunks);
+}
+
+int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                               float* H, float* amax_inout, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (nchunks < 1 || nchunks > kMaxChunks) return NVFP4_ERR_BAD_SHAPE;
+  int st = check_matrix(tokens, k, ldx, 2);
+  if (st) return st;
+  if (k % 16) return NVFP4_ERR_BAD_SHAPE;
+  if (!xs || !H) return NVFP4_ERR_NULL_ARG;
+  if (tokens == 0) return NVFP4_OK;
+  for (int c = 0; c < nchunks; ++c) {
+    if (!xs[c]) return NVFP4_ERR_NULL_ARG;
+    if ((st = check_bf16_rows(xs[c], ldx))) return st;
+  }
+  const size_t need = hessian_chunks_workspace_bytes(tokens, k, nchunks);
+  if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!workspace) return NVFP4_ERR_NULL_ARG;
+  if (!aligned16(H) || !aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  return launch_hessian_accum_chunks(xs, nchunks, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
+}
+
 int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H,
                                 float* amax_inout, void* stream) {
   int st = check_matrix(tokens, k, ldx, 2);

@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
 // latency is what counts).
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __restrict__ ws, int64_t tiles,
                                                               int64_t total, int64_t wgs, int64_t segs, int64_t groups,
-                                                              float4* __restrict__ H) {
+                                                              int nchunks, float4* __restrict__ H) {
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= groups) return;
   const int64_t s = g / kSlabGroups;
@@ -375,28 +375,31 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __res
   const int n = (int)(w_hi - w_lo + 1);
   const int seg_lo = (int)(s - (w_lo * total / wgs) / tiles);
   const int sg = (int)segs;
-  const float4* p0 = ws + ((w_lo * segs + seg_lo) * kSlabGroups + gl) * 64 + e;
-  auto at = [&](int i) -> float4 { return p0[(int64_t)(i * sg - (i ? seg_lo : 0)) * (kSlabGroups * 64)]; };
+  const int64_t chunk4 = wgs * segs * kSlabGroups * 64;       // float4 per chunk's slot set
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  int i = 0;
-  for (; i + 16 <= n; i += 16) {
-    float4 v[16];
+  for (int c = 0; c < nchunks; ++c) {                         // chunk by chunk, then workgroup order
+    const float4* p0 = ws + c * chunk4 + ((w_lo * segs + seg_lo) * kSlabGroups + gl) * 64 + e;
+    auto at = [&](int i) -> float4 { return p0[(int64_t)(i * sg - (i ? seg_lo : 0)) * (kSlabGroups * 64)]; };
+    int i = 0;
+    for (; i + 16 <= n; i += 16) {
+      float4 v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = at(i + j);
+      for (int j = 0; j < 16; ++j) v[j] = at(i + j);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s0 += (double)v[j].x;
-      s1 += (double)v[j].y;
-      s2 += (double)v[j].z;
-      s3 += (double)v[j].w;
+      for (int j = 0; j < 16; ++j) {
+        s0 += (double)v[j].x;
+        s1 += (double)v[j].y;
+        s2 += (double)v[j].z;
+        s3 += (double)v[j].w;
+      }
     }
-  }
-  for (; i < n; ++i) {
-    const float4 v = at(i);
-    s0 += (double)v.x;
-    s1 += (double)v.y;
-    s2 += (double)v.z;
-    s3 += (double)v.w;
+    for (; i < n; ++i) {
+      const float4 v = at(i);
+      s0 += (double)v.x;
+      s1 += (double)v.y;
+      s2 += (double)v.z;
+      s3 += (double)v.w;
+    }
   }
   h.x = (float)((double)h.x + s0);
   h.y = (float)((double)h.y + s1);
@@ -416,23 +419,39 @@ size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
   return a > b ? a : b;
 }
 
-static int launch_reduce(const Plan& p, int64_t k, const float* ws, float* H, hipStream_t s) {
+static int launch_reduce(const Plan& p, int64_t k, const float* ws, float* H, hipStream_t s, int nchunks = 1) {
   const int64_t groups = k / 16;
   hessian_reduce_kernel<<<(unsigned)((groups + 3) / 4), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles,
-                                                                      p.total, p.wgs, p.segs, groups,
+                                                                      p.total, p.wgs, p.segs, groups, nchunks,
                                                                       reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
 }
 
+int launch_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                                float* H, float* amax, void* workspace, hipStream_t s) {
+  const Plan p = plan(tokens, k, kTargetWgs);
+  if (p.wgs == 0 || nchunks == 0) return NVFP4_OK;
+  // One accumulate launch per chunk, each into its own partial slot set
+  // (chunk c's at ws + c * chunk_floats), then one fp64 reduce over all.
+  float* ws = static_cast<float*>(workspace);
+  const int64_t chunk_floats = p.wgs * p.segs * kSlabGroups * 256;
+  for (int c = 0; c < nchunks; ++c) {
+    hessian_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(xs[c], tokens, k, ldx, p.tiles, p.total, p.wgs,
+                                                                 p.segs, p.slabs, p.streams, ws + c * chunk_floats,
+                                                                 amax);
+    const int st = launch_status("hessian_partial_kernel");
+    if (st) return st;
+  }
+  return launch_reduce(p, k, ws, H, s, nchunks);
+}
+
 int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
                          void* workspace, hipStream_t s) {
-  const Plan p = plan(tokens, k, kTargetWgs);
-  if (p.wgs == 0) return NVFP4_OK;
-  float* ws = static_cast<float*>(workspace);
-  hessian_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
-                                                               p.slabs, p.streams, ws, amax);
-  int st = launch_status("hessian_partial_kernel");
-  return st ? st : launch_reduce(p, k, ws, H, s);
+  return launch_hessian_accum_chunks(&x, 1, tokens, k, ldx, H, amax, workspace, s);
+}
+
+size_t hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchunks) {
+  return plan_bytes(plan(tokens, k, kTargetWgs)) * (size_t)nchunks;
 }
 
 size_t hessian_plain_workspace_bytes(int64_t tokens, int64_t k) {

@@ -39,7 +39,8 @@ def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) == {
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_compute_scale2_batch", "nvfp4_hessian_workspace_bytes",
-        "nvfp4_hessian_accum", "nvfp4_hessian_accum_noalloc", "nvfp4_hessian_accum_fq", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
+        "nvfp4_hessian_accum", "nvfp4_hessian_accum_noalloc", "nvfp4_hessian_accum_fq",
+        "nvfp4_hessian_chunks_workspace_bytes", "nvfp4_hessian_accum_chunks", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
         "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant", "nvfp4_scale_sweep_ex",
         "nvfp4_quantlinear_workspace_bytes", "nvfp4_quantlinear_forward",
@@ -109,6 +110,32 @@ def test_hessian_validation(lib):
     assert f(P, 16, 32, 32, P, None, None, need, None) == NULL
     assert f(P, 0, 32, 32, P, None, None, 0, None) == OK                  # nothing to do
     assert f(P, 1 << 62, 32, 1 << 40, P, None, P, 1 << 20, None) == SHAPE   # overflow
+
+
+def test_hessian_chunks_validation(lib):
+    q = lib.nvfp4_hessian_chunks_workspace_bytes
+    one = lib.nvfp4_hessian_workspace_bytes(65536, 4096)
+    assert q(65536, 4096, 16) >= 16 * 8 * 1024 and q(65536, 4096, 16) == 16 * q(65536, 4096, 1)
+    assert q(65536, 4096, 0) == 0 and q(65536, 4096, 65) == 0 and q(0, 4096, 2) == 0 and q(16, 24, 2) == 0
+    assert q(65536, 4096, 1) <= one
+    f = lib.nvfp4_hessian_accum_chunks
+    xs = (ctypes.c_void_p * 2)(P, P + 4096)
+    need = q(16, 32, 2)
+    assert f(xs, 0, 16, 32, 32, P, None, P, need, None) == SHAPE            # nchunks < 1
+    assert f(xs, 65, 16, 32, 32, P, None, P, need, None) == SHAPE           # nchunks > 64
+    assert f(xs, 2, 16, 24, 24, P, None, P, need, None) == SHAPE            # k % 16
+    assert f(xs, 2, 16, 32, 16, P, None, P, need, None) == SHAPE            # ld < k
+    assert f(None, 2, 16, 32, 32, P, None, P, need, None) == NULL
+    assert f(xs, 2, 16, 32, 32, None, None, P, need, None) == NULL
+    bad = (ctypes.c_void_p * 2)(P, None)
+    assert f(bad, 2, 16, 32, 32, P, None, P, need, None) == NULL            # a NULL chunk
+    mis = (ctypes.c_void_p * 2)(P, P + 2)
+    assert f(mis, 2, 16, 32, 32, P, None, P, need, None) == ALIGN           # a misaligned chunk
+    assert f(xs, 2, 16, 32, 32, P, None, P, need - 1, None) == WS
+    assert f(xs, 2, 16, 32, 32, P, None, None, need, None) == NULL
+    assert f(xs, 2, 16, 32, 32, P + 4, None, P, need, None) == ALIGN        # H
+    assert f(xs, 2, 16, 32, 32, P, None, P + 8, need, None) == ALIGN        # workspace
+    assert f(xs, 2, 0, 32, 32, P, None, None, 0, None) == OK                # nothing to do
 
 
 def test_hessian_noalloc_validation(lib):

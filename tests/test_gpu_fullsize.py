@@ -61,8 +61,10 @@ def _bits(t: torch.Tensor) -> np.ndarray:
 
 class _FullH:
     """Both calibration streams' Hessians over all 2^20 tokens, computed once
-    per module: on the GPU chunk by chunk as the benchmark does, and by the
-    oracle over (token, channel) pieces of the same chunks."""
+    per module: on the GPU by one chunk-list call over the 16 resident chunks
+    as the benchmark does ("H", the sweeps' input below), and chunk by chunk
+    ("H_single"); and by the oracle over (token, channel) pieces of the same
+    chunks."""
 
     def __init__(self, pool):
         self.pool = pool
@@ -77,9 +79,10 @@ class _FullH:
         k = datagen.C4_HIDDEN if s == 0 else datagen.C4_INTER
         groups = k // 16
         tp, cp = 16384, 1024                              # piece: 16384 tokens x 64 groups
-        H = torch.zeros((groups, 16, 16), dtype=torch.float32, device=DEV)
-        amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+        H1 = torch.zeros((groups, 16, 16), dtype=torch.float32, device=DEV)
+        amax1 = torch.zeros(1, dtype=torch.float32, device=DEV)
         ws = torch.empty(nq.hessian_workspace_bytes(datagen.C4_CHUNK, k), dtype=torch.uint8, device=DEV)
+        xs = []
         ref = np.zeros((groups, 16, 16))
         amax_ref = 0.0
         pending = []                                      # (chunk, [(c0, future)])
@@ -94,18 +97,26 @@ class _FullH:
         for chunk in range(datagen.C4_TOKENS // datagen.C4_CHUNK):
             note(f"full H stream={s} k={k} chunk={chunk}")
             x = datagen.config4_chunk_torch(s, chunk, DEV)
-            nq.hessian_accum(x, H, amax=amax, workspace=ws)
+            nq.hessian_accum(x, H1, amax=amax1, workspace=ws)
             xb = _bits(x)
-            del x
+            xs.append(x)
             futs = [(c0, self.pool.submit(_pool.hessian_piece, np.ascontiguousarray(xb[t0:t0 + tp, c0:c0 + cp])))
                     for c0 in range(0, k, cp) for t0 in range(0, xb.shape[0], tp)]
             del xb
             pending.append((chunk, futs))
             if len(pending) > 2:                          # bound the host copies in flight
                 drain(pending.pop(0))
+        note(f"full H stream={s}: chunk-list call over {len(xs)} chunks")
+        H = torch.zeros((groups, 16, 16), dtype=torch.float32, device=DEV)
+        amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+        nq.hessian_accum_chunks(xs, H, amax)
+        torch.cuda.synchronize()
+        del xs
+        torch.cuda.empty_cache()
         for item in pending:
             drain(item)
-        return {"H": H, "amax": float(host(amax)[0]), "ref": ref, "amax_ref": amax_ref}
+        return {"H": H, "amax": float(host(amax)[0]), "H_single": H1, "amax_single": float(host(amax1)[0]),
+                "ref": ref, "amax_ref": amax_ref}
 
 
 @pytest.fixture(scope="module")
@@ -117,10 +128,11 @@ def full_h(pool):
 @pytest.mark.parametrize("stream_id", [0, 1])
 def test_hessian_all_chunks(full_h, stream_id):
     r = full_h(stream_id)
-    h = host(r["H"]).astype(np.float64)
-    err = rel_frobenius(h, r["ref"])
-    assert err.max() <= 1e-5, f"max rel Frobenius error {err.max():.3e} (group {int(err.argmax())})"
-    assert r["amax"] == r["amax_ref"]
+    for key, am in (("H", "amax"), ("H_single", "amax_single")):
+        h = host(r[key]).astype(np.float64)
+        err = rel_frobenius(h, r["ref"])
+        assert err.max() <= 1e-5, f"{key}: max rel Frobenius error {err.max():.3e} (group {int(err.argmax())})"
+        assert r[am] == r["amax_ref"]
 
 
 def _every_block_checks(w_bits, h32, s2, packed, codes, cost):

@@ -132,3 +132,39 @@ def test_hessian_workspace_contents_do_not_matter(fill):
             h2 = torch.zeros_like(ref)
             nq.hessian_accum(x, h2, workspace=ws)
             assert torch.equal(h, ref) and torch.equal(h2, ref) and torch.equal(h_fq, ref_fq)
+
+
+@pytest.mark.parametrize("t,k,chunks,ld", [(1000, 272, 3, None), (4096, 2048, 5, 2056), (130, 66048, 2, None),
+                                           (65536, 4096, 2, None)])
+def test_hessian_chunk_list(t, k, chunks, ld):
+    """Several chunks in one call: H against the oracle over all chunks'
+    tokens (accumulated into an existing H), within the per-chunk calls'
+    bound of them, bitwise reproducible, and amax over every chunk."""
+    note(f"hessian chunk list t={t} k={k} chunks={chunks} ld={ld}")
+    rng = np.random.default_rng(t + k + chunks)
+    bits = [datagen.f32_to_bf16_bits(rng.laplace(0, 1, (t, k)).astype(np.float32)) for _ in range(chunks)]
+    bits[1][:, :16] *= 0                                    # an all-zero group in one chunk
+    def dev(b):
+        if ld is None:
+            return to_dev_bf16(b)
+        full = np.zeros((t, ld), np.uint16)
+        full[:, :k] = b
+        return to_dev_bf16(full)[:, :k]
+    xs = [dev(b) for b in bits]
+    h0 = N.hessian(datagen.f32_to_bf16_bits(rng.standard_normal((50, k)).astype(np.float32))).astype(np.float32)
+    runs = []
+    for _ in range(2):
+        H = torch.from_numpy(h0.copy()).to(DEV)
+        amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+        nq.hessian_accum_chunks(xs, H, amax)
+        runs.append((host(H), float(host(amax)[0])))
+    assert np.array_equal(runs[0][0], runs[1][0]), "chunk-list accumulation must be bitwise reproducible"
+    allbits = np.concatenate(bits, axis=0)
+    ref = N.hessian(allbits, h_init=h0.astype(np.float64))
+    err = rel_frobenius(runs[0][0], ref)
+    assert err.max() <= TOL, f"max rel Frobenius error {err.max():.3e}"
+    assert runs[0][1] == float(np.max(np.abs(F.bf16_bits_to_f64(allbits))))
+    Hs = torch.from_numpy(h0.copy()).to(DEV)
+    for x in xs:
+        nq.hessian_accum(x, Hs)
+    assert rel_frobenius(host(Hs), ref).max() <= TOL
