@@ -207,7 +207,7 @@ def main():
 
     def hessian_stream(s, evh, b=0):
         """Calibration stream s's Hessian: one chunk-list call over its 16
-        resident chunks (one accumulate pass and one reduce), bracketed by an
+        resident chunks (one accumulate launch per chunk, one reduce), bracketed by an
         event pair on its stream."""
         evh[s][0].record(stream)
         x0 = X[s][0]
@@ -413,6 +413,8 @@ def main():
         for k, (r_, w_) in rw.items():
             if "GBps" in stage_rep[k]:
                 stage_rep[k]["frac_of_measured"] = round(stage_rep[k]["GBps"] / ceiling_for(ceil, r_, w_), 4)
+                if r_ and w_:
+                    stage_rep[k]["frac_of_copy"] = round(stage_rep[k]["GBps"] / ceil["copy_GBps"], 4)
         # each HBM stage again, over rotating distinct buffers (MALL defeated,
         # launch gaps included, one event pair per rotation)
         rot = rotated_stage_times(lib, chk, dev, stream, sptr, W, x3, s2x3, q3, P5, E5, c5, fb, ceil)
@@ -670,7 +672,10 @@ def measure_ceilings(lib, chk, dev, stream, sptr, reps=5):
                        "(copy counts read + written bytes); 5 calls each between one event pair, at "
                        f"{', '.join(str(g) for g in grids)} workgroups, best kept",
             "frac_of_measured_rule": "a stage that reads R and writes W bytes is compared with "
-                                     "(R + W) / (R / read_GBps + W / write_GBps)"}
+                                     "(R + W) / (R / read_GBps + W / write_GBps)",
+            "frac_of_copy_rule": "a stage that both reads and writes is also compared with copy_GBps: "
+                                 "interleaved read and write streams on this device reach about the copy "
+                                 "rate, not the serial read-then-write rate"}
 
 
 def ceiling_for(ceil, r, w):
@@ -813,6 +818,8 @@ def rotated_stage_times(lib, chk, dev, stream, sptr, W, x3, s2x3, q3, P5, E5, c5
         out[name] = {"ms_per_call": round(ms, 4), "rotation": what, "GBps": round(gbs, 1),
                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                      "frac_of_measured": round(gbs / ceiling_for(ceil, r_, w_), 4)}
+        if r_ and w_:
+            out[name]["frac_of_copy"] = round(gbs / ceil["copy_GBps"], 4)
     # the cast rewrote fallback nibbles in place; put the originals back is not
     # needed after this point (nothing reads P5 again)
     del xs, qs, ds, P5b, E5b, c5b

@@ -150,11 +150,14 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
                         size_t workspace_bytes, void* stream);
 
 /*
- * Step 2 over several resident chunks of one calibration stream in one call
- * (for callers that keep a stream's activations in device memory): for every
- * group g,  H[g] += sum over chunks c of X_c[:, 16g:16g+16]^T X_c[:, 16g:16g+16].
- * One accumulate pass over all chunks and one reduce, instead of a pass and a
- * reduce per chunk.  The fp32 partial sums are exactly those of one
+ * Step 2 ("Coder390 NVFP4 校正（校准）方式" §2 step 2) over several resident
+ * chunks of one calibration stream in one call (for callers that keep a
+ * stream's activations in device memory): for every group g,
+ *   H[g] += sum over chunks c of X_c[:, 16g:16g+16]^T X_c[:, 16g:16g+16].
+ * One accumulate launch per chunk, each into its own partial slots, then one
+ * reduce over all of them, instead of a reduce per chunk.  The chunks are read
+ * on `stream` after the call returns: keep them alive until that work is
+ * done.  The fp32 partial sums are exactly those of one
  * nvfp4_hessian_accum call per chunk; they are then added in fp64 (chunk by
  * chunk, each in workgroup order) and H is rounded once, so the result may
  * differ from nvfp4_hessian_accum chunk by chunk in the last bits of H (it

@@ -212,9 +212,9 @@ def hessian_chunks_workspace_bytes(tokens: int, k: int, nchunks: int) -> int:
 def hessian_accum_chunks(xs, H: torch.Tensor, amax: torch.Tensor | None = None,
                          workspace: torch.Tensor | None = None) -> torch.Tensor:
     """H += block-diagonal sum over chunks of X_c^T X_c for up to 64 bf16
-    chunks of one shape [tokens, k] (row-major, same row stride), in one
-    accumulate pass and one reduce; in place.  amax is raised to the max |x|
-    over all chunks when given."""
+    chunks of one shape [tokens, k] (row-major, same row stride): one
+    accumulate launch per chunk and one reduce over all of them; in place.
+    amax is raised to the max |x| over all chunks when given."""
     xs = list(xs)
     if not xs or len(xs) > 64:
         raise ValueError("hessian_accum_chunks takes 1 to 64 chunks")
