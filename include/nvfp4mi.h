@@ -16,7 +16,7 @@
  *   library keeps no pointer after a call returns and allocates no device
  *   memory of its own, except the hipBLASLt handle that
  *   nvfp4_quantlinear_forward creates on its first call on a device (kept
- *   until the process ends) and the static 8 MiB buffer of
+ *   until the process ends) and the static 16 MiB buffer of
  *   nvfp4_hessian_accum_noalloc (part of the library's device code, present
  *   on each device once the library runs there); scratch memory otherwise
  *   comes in as a caller-provided workspace.
@@ -185,9 +185,9 @@ int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t t
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same operation, kernels and results (bit for bit)
  * as nvfp4_hessian_accum; the fp32 partial slots live in a static device
- * buffer of 8 MiB inside the library instead (each GPU the library runs on
+ * buffer of 16 MiB inside the library instead (each GPU the library runs on
  * holds its own copy until the process ends), which fits every shape with
- * k <= 65536 and any token count.  The call allocates nothing; its first
+ * k <= 131072 and any token count.  The call allocates nothing; its first
  * call on a device looks up that device's buffer address
  * (hipGetSymbolAddress) with the device current.  All calls on one GPU share
  * the buffer: calls that overlap in time on one GPU (two host threads, or
@@ -197,7 +197,7 @@ int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t t
  * x, tokens, k, ldx, H, amax_inout, stream: as for nvfp4_hessian_accum.
  * Errors: as for nvfp4_hessian_accum without WORKSPACE, plus SCRATCH_LIMIT
  *         when nvfp4_hessian_workspace_bytes' plain-kernel share exceeds the
- *         8 MiB buffer (k > 65536), and HIP (also a failed address lookup).
+ *         16 MiB buffer (k > 131072), and HIP (also a failed address lookup).
  */
 int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
                                 float* H, float* amax_inout, void* stream);

@@ -243,7 +243,7 @@ def hessian_accum_chunks(xs, H: torch.Tensor, amax: torch.Tensor | None = None,
 
 def hessian_accum_noalloc(x: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = None) -> torch.Tensor:
     """hessian_accum without a workspace: the library's static per-device
-    buffer holds the partial slots (k <= 65536).  Calls that overlap in time
+    buffer holds the partial slots (k <= 131072).  Calls that overlap in time
     on one GPU race on that buffer."""
     _dev(x, torch.bfloat16, "x", 2)
     _dev(H, torch.float32, "H")

@@ -45,7 +45,7 @@ size_t hessian_workspace_bytes(int64_t tokens, int64_t k);
 // partial slots of the plain accumulate alone, and the static buffer that
 // holds them for nvfp4_hessian_accum_noalloc
 size_t hessian_plain_workspace_bytes(int64_t tokens, int64_t k);
-constexpr size_t kHessianScratchBytes = size_t(8) << 20;
+constexpr size_t kHessianScratchBytes = size_t(16) << 20;
 int launch_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
                                  hipStream_t s);
 int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,

@@ -3,12 +3,14 @@
 //
 // The work is HBM-bound (2 bytes read per element, 32 flops per element), so
 // the design goal is a single coalesced pass over X:
-//  * the work is cut into tiles of 64 tokens x one slab of 8 groups (128
-//    channels, 256 B of every token row).  A grid of about two workgroups per
-//    CU takes equal contiguous ranges of the slab-major tile order, so every
-//    workgroup streams the same number of bytes whatever the shape;
+//  * the work is cut into tiles of 64 tokens x one slab of 16 groups (256
+//    channels, 512 B of every token row; 8 groups in the W4A4 variant).  A
+//    grid of about two workgroups per CU takes equal contiguous ranges of the
+//    slab-major tile order, so every workgroup streams the same number of
+//    bytes whatever the shape;
 //  * tiles go through LDS (16 B per lane, coalesced rows, non-temporal loads),
-//    two tiles in flight per thread;
+//    the next tile in flight while one is consumed (32 KiB per workgroup; the
+//    W4A4 variant keeps two 16 KiB tiles in flight);
 //  * H_g = X_g^T X_g is a 16x16 contraction over tokens, done with
 //    v_mfma_f32_16x16x32_bf16.  In that instruction lane l supplies row l%16
 //    of A and column l%16 of B for K-slots 8*(l/16)..+7; for A = X_g^T and
@@ -30,7 +32,7 @@
 #include "nvfp4_device.hpp"
 
 // Partial slots of nvfp4_hessian_accum_noalloc: the plain kernel's workspace
-// for any shape with k <= 65536 (512 workgroups x 2 slabs x 8 groups x 1 KiB),
+// for any shape with k <= 131072 (512 workgroups x 2 slabs x 16 groups x 1 KiB),
 // held by each device that runs the library until the process ends.  Host
 // code never passes this name to a kernel: it uses the device address that
 // hipGetSymbolAddress returns for the current device.
@@ -40,8 +42,27 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kSlabGroups = 8;            // groups per slab
-constexpr int kSlabCols = kSlabGroups * 16;
+// Slab geometry of SG groups (SG * 16 channels, SG * 32 bytes of a token
+// row): a row is SG * 2 chunks of 16 B, one per lane, so one load pass of
+// 256 threads covers kLoadRows rows and a 64-token tile takes kUnits passes;
+// each of the 4 waves owns SG / 4 groups of the slab.
+template <int SG>
+struct Slab {
+  static constexpr int kGroups = SG;
+  static constexpr int kCols = SG * 16;
+  static constexpr int kChunks = SG * 2;
+  static constexpr int kLoadRows = 256 / kChunks;
+  static constexpr int kUnits = 64 / kLoadRows;
+  static constexpr int kWaveGroups = SG / 4;
+};
+// The plain kernel: 16-group slabs, one tile in flight (measured on MI355X
+// against 8-group slabs with two 16 KiB tiles in flight: 2647 against 2659 us
+// per 16-chunk call alone, 6.16-6.17 against 6.21-6.25 ms per benchmark
+// step; two 32 KiB tiles in flight need more than 128 VGPRs).  The W4A4
+// kernel keeps 8-group slabs: its two LDS tile buffers and four workgroups
+// per CU would not fit in LDS with 16.
+constexpr int kPlainSG = 16;
+constexpr int kFqSG = 8;
 constexpr int kTile = 64;                 // tokens per LDS tile
 constexpr int kThreads = 256;
 constexpr int kTargetWgs = 512;           // two workgroups on each of 256 CUs (measured best)
@@ -64,12 +85,13 @@ __host__ __device__ inline int64_t cdiv(int64_t n, int64_t d) { return (n + d - 
 // two workgroups per CU, evenly spread, streams fastest (shapes that leave
 // some CUs with a third workgroup run 15-20% slower).
 struct Plan {
-  int64_t slabs, tiles, total, wgs, segs, streams;
+  int64_t slabs, tiles, total, wgs, segs, streams, sg;
 };
 
-Plan plan(int64_t tokens, int64_t k, int64_t target) {
+Plan plan(int64_t tokens, int64_t k, int64_t target, int sg) {
   Plan p;
-  p.slabs = cdiv(k / 16, kSlabGroups);
+  p.sg = sg;
+  p.slabs = cdiv(k / 16, sg);
   p.tiles = cdiv(tokens, kTile);
   p.total = p.slabs * p.tiles;
   p.streams = p.slabs < target ? target / p.slabs : 1;
@@ -113,6 +135,7 @@ __device__ __forceinline__ uint32_t pair_max(uint32_t p) {
 // block maxima (the fused amax of the unquantized input).
 template <int QM>
 __device__ __forceinline__ void fake_quant_tile(uint4* v, const FqState& q, u16x2& amx) {
+  static_assert(Slab<kFqSG>::kUnits == 4, "four 8-value chunks per lane and tile");
   uint32_t P[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -151,7 +174,8 @@ __device__ __forceinline__ void fake_quant_tile(uint4* v, const FqState& q, u16x
   }
 }
 
-// LDS tile buffers: 1 for the plain kernel, 2 for the fake-quant kernel.
+// LDS tile buffers and register tiles in flight: 1 for the plain kernel, 2
+// for the fake-quant kernel.
 template <int QM>
 constexpr int kTileBufs = QM >= 0 ? 2 : 1;
 
@@ -160,11 +184,13 @@ constexpr int kTileBufs = QM >= 0 ? 2 : 1;
 // (W4A4 calibration): H += Xh^T Xh with Xh = DQ(Q(X)) at the activations'
 // tensor scale, quantized in registers between the load and the LDS store,
 // E2M1 mode QM.  Returns the lane's packed running max |x|.
-template <int QM>
+template <int QM, int SG>
 __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, int64_t tokens, int64_t k, int64_t ldx,
                                               int64_t tiles, int64_t total, int64_t wgs, int64_t segs, int64_t slabs,
                                               int64_t streams, float* __restrict__ ws, bool want_amax,
                                               uint16_t* lds_tiles, const FqState& fq) {
+  using L = Slab<SG>;
+  constexpr int NF = kTileBufs<QM>;                    // register tiles in flight
   int tb = 0;                                          // tiles consumed (LDS buffer parity)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,11 +204,11 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
   const int64_t f1 = (w + 1) * total / wgs;
   const int64_t first_slab = f0 / tiles;
 
-  // loader: thread owns chunk j = tid%16 of rows tid/16 + 16*i
-  const int lj = tid & 15;
-  const int lr = tid >> 4;
+  // loader: thread owns chunk j = tid % kChunks of rows tid / kChunks + kLoadRows * u
+  const int lj = tid & (L::kChunks - 1);
+  const int lr = tid / L::kChunks;
 
-  // MFMA reader: this wave owns groups 2*wave and 2*wave+1 of the slab
+  // MFMA reader: this wave owns groups kWaveGroups * wave + 0, 1, ... of the slab
   const int q = lane >> 4;
   const int ch = lane & 15;
 
@@ -193,16 +219,16 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
     const int64_t t0 = f - slab * tiles;
     const int64_t t1 = (f1 - slab * tiles) < tiles ? (f1 - slab * tiles) : tiles;
     const int ntiles = (int)(t1 - t0);
-    const int64_t gcol = slab * kSlabCols + lj * 8;
+    const int64_t gcol = slab * L::kCols + lj * 8;
     const bool col_ok = gcol < k;          // k % 16 == 0, so a chunk is all-in or all-out
 
-    floatx4 acc[2];
-    acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[L::kWaveGroups];
+#pragma unroll
+    for (int i = 0; i < L::kWaveGroups; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // two tiles in flight per thread: tile i+2 is requested as soon as tile i
-    // sits in LDS
-    uint4 bufA[4], bufB[4];
+    // NF tiles in flight per thread: tile i + NF is requested as soon as tile
+    // i sits in LDS
+    uint4 bufs[NF][L::kUnits];
     // per-lane part of the address; the tile's row offset is wave-uniform
     const int64_t lane_off = (int64_t)lr * ldx + gcol;
     auto load_tile = [&](uint4* buf, int i) {
@@ -210,11 +236,11 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
       const int64_t rows_left = tokens - r0;           // rows lr + 16u < rows_left exist
       const uint16_t* base = x + r0 * ldx;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (col_ok && lr + 16 * u < rows_left) {
+      for (int u = 0; u < L::kUnits; ++u) {
+        if (col_ok && lr + L::kLoadRows * u < rows_left) {
           // X is read exactly once: a non-temporal load keeps it from
           // displacing cached data (measured 10% faster than a plain load)
-          buf[u] = ld_nt4(base + lane_off + (int64_t)(16 * u) * ldx);
+          buf[u] = ld_nt4(base + lane_off + (int64_t)(L::kLoadRows * u) * ldx);
         } else {
           buf[u] = make_uint4(0u, 0u, 0u, 0u);
         }
@@ -226,18 +252,18 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
       // (fake-quant kernel, measured 2-6% faster there): the barrier after
       // this write also retires the reads of the buffer written next
       if constexpr (kTileBufs<QM> == 1) __syncthreads();
-      uint16_t* tile = lds_tiles + (tb % kTileBufs<QM>) * (kTile * kSlabCols);
+      uint16_t* tile = lds_tiles + (tb % kTileBufs<QM>) * (kTile * L::kCols);
       ++tb;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int R = lr + 16 * u;
-        *reinterpret_cast<uint4*>(&tile[R * kSlabCols + swz(lj, R) * 8]) = buf[u];
+      for (int u = 0; u < L::kUnits; ++u) {
+        const int R = lr + L::kLoadRows * u;
+        *reinterpret_cast<uint4*>(&tile[R * L::kCols + swz(lj, R) * 8]) = buf[u];
       }
       __syncthreads();
-      if (i + 2 < ntiles) load_tile(buf, i + 2);
+      if (i + NF < ntiles) load_tile(buf, i + NF);
 #pragma unroll
-      for (int gsub = 0; gsub < 2; ++gsub) {
-        const int gl = 2 * wave + gsub;               // group within the slab
+      for (int gsub = 0; gsub < L::kWaveGroups; ++gsub) {
+        const int gl = L::kWaveGroups * wave + gsub;   // group within the slab
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           // Two transposing reads: lane jj of each 16-lane group fetches 4
@@ -251,9 +277,9 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
           const int c4 = gl * 16 + 4 * (jj & 3);
           const int R0 = 32 * m + 8 * q + (jj >> 2);
           const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)&tile[R0 * kSlabCols + swz(c4 >> 3, R0) * 8 + (c4 & 7)]);
+              (__attribute__((address_space(3))) s16x4*)&tile[R0 * L::kCols + swz(c4 >> 3, R0) * 8 + (c4 & 7)]);
           const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)&tile[(R0 + 4) * kSlabCols + swz(c4 >> 3, R0 + 4) * 8 +
+              (__attribute__((address_space(3))) s16x4*)&tile[(R0 + 4) * L::kCols + swz(c4 >> 3, R0 + 4) * 8 +
                                                               (c4 & 7)]);
           const u16x8 v = __builtin_bit_cast(u16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
           if (QM < 0 && want_amax) {
@@ -266,19 +292,21 @@ __device__ __forceinline__ u16x2 partial_body(const uint16_t* __restrict__ x, in
       }
     };
 
-    load_tile(bufA, 0);
-    if (ntiles > 1) load_tile(bufB, 1);
-    for (int i = 0; i < ntiles; i += 2) {
-      consume(bufA, i);
-      if (i + 1 < ntiles) consume(bufB, i + 1);
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      if (j < ntiles) load_tile(bufs[j], j);
+    for (int i = 0; i < ntiles; i += NF) {
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        if (i + j < ntiles) consume(bufs[j], i + j);
     }
 
     // partial slot (w, slab - first_slab); lane holds C[4q + r][ch]
-    float* slot = ws + ((w * segs + (slab - first_slab)) * kSlabGroups) * 256;
+    float* slot = ws + ((w * segs + (slab - first_slab)) * SG) * 256;
 #pragma unroll
-    for (int gsub = 0; gsub < 2; ++gsub) {
-      const int gl = 2 * wave + gsub;
-      if (slab * kSlabGroups + gl < groups) {
+    for (int gsub = 0; gsub < L::kWaveGroups; ++gsub) {
+      const int gl = L::kWaveGroups * wave + gsub;
+      if (slab * SG + gl < groups) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) slot[gl * 256 + (4 * q + r) * 16 + ch] = acc[gsub][r];
       }
@@ -305,20 +333,22 @@ __device__ __forceinline__ void reduce_amax(u16x2 amx, float* amax) {
   }
 }
 
-__global__ __launch_bounds__(kThreads, 6) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
+// At most 128 VGPRs (it takes 104): two of its workgroups stay resident
+// beside a 256-VGPR sweep wave on every SIMD.
+__global__ __launch_bounds__(kThreads, 4) void hessian_partial_kernel(const uint16_t* __restrict__ x, int64_t tokens,
                                                                        int64_t k, int64_t ldx, int64_t tiles,
                                                                        int64_t total, int64_t wgs, int64_t segs,
                                                                        int64_t slabs, int64_t streams,
                                                                        float* __restrict__ ws, float* amax) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kSlabCols];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * Slab<kPlainSG>::kCols];
   // Beside a VALU-bound kernel on another stream (a sweep) this kernel's
   // waves win instruction arbitration: the memory stream is what bounds it,
   // and a pure-FMA kernel at one wave per SIMD slowed it by half at the
   // default priority, by 2% at this one.  Alone it changes nothing.
   __builtin_amdgcn_s_setprio(3);
   const FqState q{};
-  const u16x2 amx = partial_body<-1>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws,
-                                     amax != nullptr, tile, q);
+  const u16x2 amx = partial_body<-1, kPlainSG>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws,
+                                               amax != nullptr, tile, q);
   if (amax) reduce_amax(amx, amax);
 }
 
@@ -331,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
                                                                           float* __restrict__ ws, float* amax,
                                                                           const float* __restrict__ scale2,
                                                                           int force_exact) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2 * kTile * kSlabCols];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2 * kTile * Slab<kFqSG>::kCols];
   __shared__ CodeTables t;
   __shared__ int32_t tp[128];
   FqState q;
@@ -344,11 +374,11 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
   const int mode = table_mode(t);
   u16x2 amx;
   if (mode == 0)
-    amx = partial_body<0>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
+    amx = partial_body<0, kFqSG>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
   else if (mode == 1)
-    amx = partial_body<1>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
+    amx = partial_body<1, kFqSG>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
   else
-    amx = partial_body<2>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
+    amx = partial_body<2, kFqSG>(x, tokens, k, ldx, tiles, total, wgs, segs, slabs, streams, ws, false, tile, q);
   if (amax) reduce_amax(amx, amax);
 }
 
@@ -358,13 +388,14 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
 // over every owning workgroup, its H element loaded up front, so the kernel
 // is one round of loads (it sits between two accumulate passes, where its
 // latency is what counts).
+template <int SG>
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __restrict__ ws, int64_t tiles,
                                                               int64_t total, int64_t wgs, int64_t segs, int64_t groups,
                                                               int nchunks, float4* __restrict__ H) {
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= groups) return;
-  const int64_t s = g / kSlabGroups;
-  const int gl = (int)(g % kSlabGroups);
+  const int64_t s = g / SG;
+  const int gl = (int)(g % SG);
   const int e = threadIdx.x & 63;
   float4 h = H[g * 64 + e];
   // owning workgroups of slab s: w_lo .. w_hi (all with non-empty ranges);
@@ -375,11 +406,11 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __res
   const int n = (int)(w_hi - w_lo + 1);
   const int seg_lo = (int)(s - (w_lo * total / wgs) / tiles);
   const int sg = (int)segs;
-  const int64_t chunk4 = wgs * segs * kSlabGroups * 64;       // float4 per chunk's slot set
+  const int64_t chunk4 = wgs * segs * SG * 64;                // float4 per chunk's slot set
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
   for (int c = 0; c < nchunks; ++c) {                         // chunk by chunk, then workgroup order
-    const float4* p0 = ws + c * chunk4 + ((w_lo * segs + seg_lo) * kSlabGroups + gl) * 64 + e;
-    auto at = [&](int i) -> float4 { return p0[(int64_t)(i * sg - (i ? seg_lo : 0)) * (kSlabGroups * 64)]; };
+    const float4* p0 = ws + c * chunk4 + ((w_lo * segs + seg_lo) * SG + gl) * 64 + e;
+    auto at = [&](int i) -> float4 { return p0[(int64_t)(i * sg - (i ? seg_lo : 0)) * (SG * 64)]; };
     int i = 0;
     for (; i + 16 <= n; i += 16) {
       float4 v[16];
@@ -410,31 +441,32 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __res
 
 }  // namespace
 
-static size_t plan_bytes(const Plan& p) { return (size_t)(p.wgs * p.segs) * kSlabGroups * 256u * sizeof(float); }
+static size_t plan_bytes(const Plan& p) { return (size_t)(p.wgs * p.segs * p.sg) * 256u * sizeof(float); }
 
 // one query for both variants: the larger of their partial buffers
 size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
-  const size_t a = plan_bytes(plan(tokens, k, kTargetWgs));
-  const size_t b = plan_bytes(plan(tokens, k, kTargetWgsFq));
+  const size_t a = plan_bytes(plan(tokens, k, kTargetWgs, kPlainSG));
+  const size_t b = plan_bytes(plan(tokens, k, kTargetWgsFq, kFqSG));
   return a > b ? a : b;
 }
 
+template <int SG>
 static int launch_reduce(const Plan& p, int64_t k, const float* ws, float* H, hipStream_t s, int nchunks = 1) {
   const int64_t groups = k / 16;
-  hessian_reduce_kernel<<<(unsigned)((groups + 3) / 4), 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles,
-                                                                      p.total, p.wgs, p.segs, groups, nchunks,
-                                                                      reinterpret_cast<float4*>(H));
+  hessian_reduce_kernel<SG><<<(unsigned)((groups + 3) / 4), 256, 0, s>>>(reinterpret_cast<const float4*>(ws),
+                                                                          p.tiles, p.total, p.wgs, p.segs, groups,
+                                                                          nchunks, reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
 }
 
 int launch_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
                                 float* H, float* amax, void* workspace, hipStream_t s) {
-  const Plan p = plan(tokens, k, kTargetWgs);
+  const Plan p = plan(tokens, k, kTargetWgs, kPlainSG);
   if (p.wgs == 0 || nchunks == 0) return NVFP4_OK;
   // One accumulate launch per chunk, each into its own partial slot set
   // (chunk c's at ws + c * chunk_floats), then one fp64 reduce over all.
   float* ws = static_cast<float*>(workspace);
-  const int64_t chunk_floats = p.wgs * p.segs * kSlabGroups * 256;
+  const int64_t chunk_floats = p.wgs * p.segs * kPlainSG * 256;
   for (int c = 0; c < nchunks; ++c) {
     hessian_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(xs[c], tokens, k, ldx, p.tiles, p.total, p.wgs,
                                                                  p.segs, p.slabs, p.streams, ws + c * chunk_floats,
@@ -442,7 +474,7 @@ int launch_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t 
     const int st = launch_status("hessian_partial_kernel");
     if (st) return st;
   }
-  return launch_reduce(p, k, ws, H, s, nchunks);
+  return launch_reduce<kPlainSG>(p, k, ws, H, s, nchunks);
 }
 
 int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax,
@@ -451,11 +483,11 @@ int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t l
 }
 
 size_t hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchunks) {
-  return plan_bytes(plan(tokens, k, kTargetWgs)) * (size_t)nchunks;
+  return plan_bytes(plan(tokens, k, kTargetWgs, kPlainSG)) * (size_t)nchunks;
 }
 
 size_t hessian_plain_workspace_bytes(int64_t tokens, int64_t k) {
-  return plan_bytes(plan(tokens, k, kTargetWgs));
+  return plan_bytes(plan(tokens, k, kTargetWgs, kPlainSG));
 }
 
 // Device address of `scratch` per device, looked up once per device with
@@ -493,14 +525,14 @@ int launch_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, i
 
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
                             float* amax, void* workspace, hipStream_t s) {
-  const Plan p = plan(tokens, k, kTargetWgsFq);
+  const Plan p = plan(tokens, k, kTargetWgsFq, kFqSG);
   if (p.wgs == 0) return NVFP4_OK;
   float* ws = static_cast<float*>(workspace);
   hessian_fq_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
                                                                   p.slabs, p.streams, ws, amax, scale2,
                                                                   force_exact_flag());
   int st = launch_status("hessian_fq_partial_kernel");
-  return st ? st : launch_reduce(p, k, ws, H, s);
+  return st ? st : launch_reduce<kFqSG>(p, k, ws, H, s);
 }
 
 }  // namespace nvfp4

@@ -150,10 +150,10 @@ def test_hessian_noalloc_validation(lib):
     assert f(P, 16, 32, 32, P + 4, None, None) == ALIGN                   # H
     assert f(P, 0, 32, 32, P, None, None) == OK                           # nothing to do
     assert f(P, 1 << 62, 32, 1 << 40, P, None, None) == SHAPE             # overflow
-    # beyond the static buffer: 513 slabs of 8 groups need three partial
-    # slots per workgroup (12 MiB); rejected before any HIP call
-    assert f(P, 65536, 65552, 65552, P, None, None) == SCRATCH
-    assert f(P, 64, 65552, 65552, P, None, None) == SCRATCH
+    # beyond the static buffer: 513 slabs of 16 groups need three partial
+    # slots for each of 512 workgroups (24 MiB); rejected before any HIP call
+    assert f(P, 65536, 131088, 131088, P, None, None) == SCRATCH
+    assert f(P, 64, 131088, 131088, P, None, None) == SCRATCH
 
 
 def test_hessian_fq_validation(lib):
