@@ -383,21 +383,25 @@ __global__ __launch_bounds__(kThreads, 4) void hessian_fq_partial_kernel(const u
 }
 
 // H[g] += sum of the partials of group g over the workgroups whose range
-// touches g's slab, in fp64 and in workgroup order (deterministic).  One wave
-// per group (four groups per workgroup): lane e sums float4 e of the group
-// over every owning workgroup, its H element loaded up front, so the kernel
-// is one round of loads (it sits between two accumulate passes, where its
-// latency is what counts).
+// touches g's slab (with nchunks slot sets, those of every chunk), in fp64
+// and in a fixed order (deterministic).  One workgroup per group: the
+// (chunk, owner) items are cut into four contiguous ranges, one per wave,
+// each lane summing float4 e of the group over its wave's range (16 loads in
+// flight); wave 0 then adds H and the four sums in wave order.  (One wave per
+// group had left a 16-chunk call's reduce latency-bound: 55 us at
+// K = 12288.)
 template <int SG>
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __restrict__ ws, int64_t tiles,
                                                               int64_t total, int64_t wgs, int64_t segs, int64_t groups,
                                                               int nchunks, float4* __restrict__ H) {
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= groups) return;
+  __shared__ double part[3][4][64];                           // the sums of waves 1..3
+  const int64_t g = blockIdx.x;
   const int64_t s = g / SG;
   const int gl = (int)(g % SG);
+  const int wave = threadIdx.x >> 6;
   const int e = threadIdx.x & 63;
-  float4 h = H[g * 64 + e];
+  float4 h = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (wave == 0) h = H[g * 64 + e];
   // owning workgroups of slab s: w_lo .. w_hi (all with non-empty ranges);
   // only w_lo's range can start before slab s, so only its slot for s can
   // sit past segment 0
@@ -407,36 +411,59 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float4* __res
   const int seg_lo = (int)(s - (w_lo * total / wgs) / tiles);
   const int sg = (int)segs;
   const int64_t chunk4 = wgs * segs * SG * 64;                // float4 per chunk's slot set
+  const float4* p0 = ws + ((w_lo * segs + seg_lo) * SG + gl) * 64 + e;
+  // items it = c * n + i (owner i of chunk c), chunk by chunk, then
+  // workgroup order; this wave's are [it0, it1) (at most 64 * 512 items)
+  const int items = nchunks * n;
+  const int it0 = items * wave / 4, it1 = items * (wave + 1) / 4;
+  int c = it0 / n, i = it0 - c * n;
+  auto next = [&]() -> const float4* {
+    const float4* q = p0 + c * chunk4 + (int64_t)(i * sg - (i ? seg_lo : 0)) * (SG * 64);
+    if (++i == n) { i = 0; ++c; }
+    return q;
+  };
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  for (int c = 0; c < nchunks; ++c) {                         // chunk by chunk, then workgroup order
-    const float4* p0 = ws + c * chunk4 + ((w_lo * segs + seg_lo) * SG + gl) * 64 + e;
-    auto at = [&](int i) -> float4 { return p0[(int64_t)(i * sg - (i ? seg_lo : 0)) * (SG * 64)]; };
-    int i = 0;
-    for (; i + 16 <= n; i += 16) {
-      float4 v[16];
+  int it = it0;
+  for (; it + 16 <= it1; it += 16) {
+    float4 v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = at(i + j);
+    for (int j = 0; j < 16; ++j) v[j] = *next();
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s0 += (double)v[j].x;
-        s1 += (double)v[j].y;
-        s2 += (double)v[j].z;
-        s3 += (double)v[j].w;
-      }
-    }
-    for (; i < n; ++i) {
-      const float4 v = at(i);
-      s0 += (double)v.x;
-      s1 += (double)v.y;
-      s2 += (double)v.z;
-      s3 += (double)v.w;
+    for (int j = 0; j < 16; ++j) {
+      s0 += (double)v[j].x;
+      s1 += (double)v[j].y;
+      s2 += (double)v[j].z;
+      s3 += (double)v[j].w;
     }
   }
-  h.x = (float)((double)h.x + s0);
-  h.y = (float)((double)h.y + s1);
-  h.z = (float)((double)h.z + s2);
-  h.w = (float)((double)h.w + s3);
-  H[g * 64 + e] = h;
+  for (; it < it1; ++it) {
+    const float4 v = *next();
+    s0 += (double)v.x;
+    s1 += (double)v.y;
+    s2 += (double)v.z;
+    s3 += (double)v.w;
+  }
+  if (wave > 0) {
+    part[wave - 1][0][e] = s0;
+    part[wave - 1][1][e] = s1;
+    part[wave - 1][2][e] = s2;
+    part[wave - 1][3][e] = s3;
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      s0 += part[w][0][e];
+      s1 += part[w][1][e];
+      s2 += part[w][2][e];
+      s3 += part[w][3][e];
+    }
+    h.x = (float)((double)h.x + s0);
+    h.y = (float)((double)h.y + s1);
+    h.z = (float)((double)h.z + s2);
+    h.w = (float)((double)h.w + s3);
+    H[g * 64 + e] = h;
+  }
 }
 
 }  // namespace
@@ -453,9 +480,9 @@ size_t hessian_workspace_bytes(int64_t tokens, int64_t k) {
 template <int SG>
 static int launch_reduce(const Plan& p, int64_t k, const float* ws, float* H, hipStream_t s, int nchunks = 1) {
   const int64_t groups = k / 16;
-  hessian_reduce_kernel<SG><<<(unsigned)((groups + 3) / 4), 256, 0, s>>>(reinterpret_cast<const float4*>(ws),
-                                                                          p.tiles, p.total, p.wgs, p.segs, groups,
-                                                                          nchunks, reinterpret_cast<float4*>(H));
+  hessian_reduce_kernel<SG><<<(unsigned)groups, 256, 0, s>>>(reinterpret_cast<const float4*>(ws), p.tiles, p.total,
+                                                             p.wgs, p.segs, groups, nchunks,
+                                                             reinterpret_cast<float4*>(H));
   return launch_status("hessian_reduce_kernel");
 }
 
