@@ -135,7 +135,7 @@ def test_hessian_workspace_contents_do_not_matter(fill):
 
 
 @pytest.mark.parametrize("t,k,chunks,ld", [(1000, 272, 3, None), (4096, 2048, 5, 2056), (130, 66048, 2, None),
-                                           (65536, 4096, 2, None)])
+                                           (65536, 4096, 2, None), (64, 512, 64, None), (7, 16, 2, None)])
 def test_hessian_chunk_list(t, k, chunks, ld):
     """Several chunks in one call: H against the oracle over all chunks'
     tokens (accumulated into an existing H), within the per-chunk calls'
@@ -168,3 +168,13 @@ def test_hessian_chunk_list(t, k, chunks, ld):
     for x in xs:
         nq.hessian_accum(x, Hs)
     assert rel_frobenius(host(Hs), ref).max() <= TOL
+
+
+def test_hessian_chunk_list_empty_chunks():
+    """Chunks without tokens leave H and amax as they were."""
+    note("hessian chunk list: empty chunks")
+    xs = [torch.empty((0, 64), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    H = torch.full((4, 16, 16), 1.5, dtype=torch.float32, device=DEV)
+    amax = torch.full((1,), 2.0, dtype=torch.float32, device=DEV)
+    nq.hessian_accum_chunks(xs, H, amax)
+    assert torch.equal(H, torch.full_like(H, 1.5)) and float(host(amax)[0]) == 2.0
