@@ -90,7 +90,7 @@ const char* nvfp4_status_string(int status);
  *            accumulator, so it must not alias x.
  * amax_out   device float[1] or NULL: receives amax.
  * Errors: NULL_ARG (x with n > 0, scale2_out), BAD_SHAPE (n < 0),
- *         MISALIGNED (x), HIP.
+ *         MISALIGNED (x; scale2_out or amax_out not 4-byte aligned), HIP.
  */
 int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out,
                          float* amax_out, void* stream);
@@ -143,7 +143,7 @@ size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k);
  *            scratch.
  * Errors: NULL_ARG, BAD_SHAPE (tokens < 0, k <= 0, k % 16, ldx < k),
  *         MISALIGNED (x or ldx not 16-byte aligned rows; H or workspace not
- *         16-byte aligned), WORKSPACE, HIP.
+ *         16-byte aligned; amax_inout not 4-byte aligned), WORKSPACE, HIP.
  */
 int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
                         float* H, float* amax_inout, void* workspace,
@@ -323,7 +323,8 @@ int nvfp4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scal
  * fallback_blocks_out [groups] int64 out or NULL: number of 32-element MX
  *          blocks per group that took the fallback (0 = lossless group).
  * Errors: NULL_ARG, BAD_SHAPE (sizes <= 0, k % 32), BAD_INPUT, MISALIGNED
- *         (packed/e8m0/codes_out not 16-byte aligned), HIP.
+ *         (packed/e8m0/codes_out not 16-byte aligned, scale2_out not 4-byte
+ *         or fallback_blocks_out not 8-byte aligned), HIP.
  */
 int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups,
                         int64_t mats_per_group, int64_t rows, int64_t k,
@@ -344,7 +345,8 @@ int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups,
  * x [n] bf16, contiguous, 16-byte aligned (n may be 0: s = 0).
  * scale_out device float[1] (also the running accumulator: must not alias x);
  * amax_out device float[1] or NULL.
- * Errors: NULL_ARG (x with n > 0, scale_out), BAD_SHAPE (n < 0), MISALIGNED, HIP.
+ * Errors: NULL_ARG (x with n > 0, scale_out), BAD_SHAPE (n < 0), MISALIGNED
+ *         (x; scale_out or amax_out not 4-byte aligned), HIP.
  */
 int fp8e4m3_compute_scale(const uint16_t* x, int64_t n, float* scale_out,
                           float* amax_out, void* stream);

@@ -70,6 +70,7 @@ int nvfp4_compute_scale2(const uint16_t* x, int64_t n, float* scale2_out, float*
   if (n < 0 || !mul_fits(n, 2)) return NVFP4_ERR_BAD_SHAPE;
   if (!scale2_out || (n > 0 && !x)) return NVFP4_ERR_NULL_ARG;
   if (n > 0 && !aligned16(x)) return NVFP4_ERR_MISALIGNED;
+  if (!aligned4(scale2_out) || (amax_out && !aligned4(amax_out))) return NVFP4_ERR_MISALIGNED;   // atomic targets
   return launch_compute_scale2(x, n, scale2_out, amax_out, as_stream(stream));
 }
 
@@ -93,7 +94,7 @@ size_t nvfp4_hessian_workspace_bytes(int64_t tokens, int64_t k) {
 
 // Shared validation of the two Hessian entry points.
 static int check_hessian(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* H,
-                         const void* workspace, size_t workspace_bytes) {
+                         const float* amax, const void* workspace, size_t workspace_bytes) {
   int st = check_matrix(tokens, k, ldx, 2);
   if (st) return st;
   if (k % 16) return NVFP4_ERR_BAD_SHAPE;
@@ -104,12 +105,13 @@ static int check_hessian(const uint16_t* x, int64_t tokens, int64_t k, int64_t l
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (need && !workspace) return NVFP4_ERR_NULL_ARG;
   if (!aligned16(H) || !aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  if (amax && !aligned4(amax)) return NVFP4_ERR_MISALIGNED;                                   // atomic target
   return NVFP4_OK;
 }
 
 int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H, float* amax_inout,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_hessian(x, tokens, k, ldx, H, workspace, workspace_bytes);
+  int st = check_hessian(x, tokens, k, ldx, H, amax_inout, workspace, workspace_bytes);
   if (st || tokens == 0) return st;
   return launch_hessian_accum(x, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
 }
@@ -137,6 +139,7 @@ int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t t
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (!workspace) return NVFP4_ERR_NULL_ARG;
   if (!aligned16(H) || !aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  if (amax_inout && !aligned4(amax_inout)) return NVFP4_ERR_MISALIGNED;
   return launch_hessian_accum_chunks(xs, nchunks, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
 }
 
@@ -148,14 +151,14 @@ int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, in
   if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL_ARG;
   if (tokens == 0) return NVFP4_OK;
   if ((st = check_bf16_rows(x, ldx))) return st;
-  if (!aligned16(H)) return NVFP4_ERR_MISALIGNED;
+  if (!aligned16(H) || (amax_inout && !aligned4(amax_inout))) return NVFP4_ERR_MISALIGNED;
   if (hessian_plain_workspace_bytes(tokens, k) > kHessianScratchBytes) return NVFP4_ERR_SCRATCH_LIMIT;
   return launch_hessian_accum_noalloc(x, tokens, k, ldx, H, amax_inout, as_stream(stream));
 }
 
 int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
                            float* amax_inout, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_hessian(x, tokens, k, ldx, H, workspace, workspace_bytes);
+  int st = check_hessian(x, tokens, k, ldx, H, amax_inout, workspace, workspace_bytes);
   if (st) return st;
   if (!scale2) return NVFP4_ERR_NULL_ARG;
   if (tokens == 0) return NVFP4_OK;
@@ -258,6 +261,8 @@ int mxfp4_to_nvfp4_cast(uint8_t* packed, const uint8_t* e8m0, int64_t groups, in
   if (!scale2_out) return NVFP4_ERR_NULL_ARG;
   if (rows > 0 && (!packed || !e8m0 || !codes_out)) return NVFP4_ERR_NULL_ARG;
   if (rows > 0 && (!aligned16(packed) || !aligned16(e8m0) || !aligned16(codes_out))) return NVFP4_ERR_MISALIGNED;
+  if (!aligned4(scale2_out) || (fallback_blocks_out && !aligned8(fallback_blocks_out)))          // atomic targets
+    return NVFP4_ERR_MISALIGNED;
   return launch_mx_cast(packed, e8m0, groups, mats_per_group, rows, k, codes_out, scale2_out,
                         fallback_blocks_out, as_stream(stream));
 }
@@ -266,6 +271,7 @@ int fp8e4m3_compute_scale(const uint16_t* x, int64_t n, float* scale_out, float*
   if (n < 0 || !mul_fits(n, 2)) return NVFP4_ERR_BAD_SHAPE;
   if (!scale_out || (n > 0 && !x)) return NVFP4_ERR_NULL_ARG;
   if (n > 0 && !aligned16(x)) return NVFP4_ERR_MISALIGNED;
+  if (!aligned4(scale_out) || (amax_out && !aligned4(amax_out))) return NVFP4_ERR_MISALIGNED;    // atomic targets
   return launch_fp8_scale(x, n, scale_out, amax_out, as_stream(stream));
 }
 

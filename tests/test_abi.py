@@ -67,6 +67,8 @@ def test_compute_scale2_validation(lib):
     assert lib.nvfp4_compute_scale2(None, 16, P, None, None) == NULL
     assert lib.nvfp4_compute_scale2(P, 16, None, None, None) == NULL
     assert lib.nvfp4_compute_scale2(P + 2, 16, P, None, None) == ALIGN
+    assert lib.nvfp4_compute_scale2(P, 16, P + 2, None, None) == ALIGN      # scale2_out: an atomic target
+    assert lib.nvfp4_compute_scale2(P, 16, P, P + 1, None) == ALIGN         # amax_out
 
 
 def test_compute_scale2_batch_validation(lib):
@@ -105,6 +107,7 @@ def test_hessian_validation(lib):
     assert f(P, 16, 32, 36, P, None, P, 1 << 20, None) == ALIGN           # row stride not 16 B
     assert f(P, 16, 32, 32, P + 4, None, P, 1 << 20, None) == ALIGN       # H
     assert f(P, 16, 32, 32, P, None, P + 8, 1 << 20, None) == ALIGN       # workspace
+    assert f(P, 16, 32, 32, P, P + 2, P, 1 << 20, None) == ALIGN          # amax: an atomic target
     need = lib.nvfp4_hessian_workspace_bytes(16, 32)
     assert f(P, 16, 32, 32, P, None, P, need - 1, None) == WS
     assert f(P, 16, 32, 32, P, None, None, need, None) == NULL
@@ -135,6 +138,7 @@ def test_hessian_chunks_validation(lib):
     assert f(xs, 2, 16, 32, 32, P, None, None, need, None) == NULL
     assert f(xs, 2, 16, 32, 32, P + 4, None, P, need, None) == ALIGN        # H
     assert f(xs, 2, 16, 32, 32, P, None, P + 8, need, None) == ALIGN        # workspace
+    assert f(xs, 2, 16, 32, 32, P, P + 2, P, need, None) == ALIGN           # amax
     assert f(xs, 2, 0, 32, 32, P, None, None, 0, None) == OK                # nothing to do
 
 
@@ -148,6 +152,7 @@ def test_hessian_noalloc_validation(lib):
     assert f(P + 2, 16, 32, 32, P, None, None) == ALIGN
     assert f(P, 16, 32, 36, P, None, None) == ALIGN                       # row stride not 16 B
     assert f(P, 16, 32, 32, P + 4, None, None) == ALIGN                   # H
+    assert f(P, 16, 32, 32, P, P + 2, None) == ALIGN                      # amax
     assert f(P, 0, 32, 32, P, None, None) == OK                           # nothing to do
     assert f(P, 1 << 62, 32, 1 << 40, P, None, None) == SHAPE             # overflow
     # beyond the static buffer: 513 slabs of 16 groups need three partial
@@ -167,6 +172,7 @@ def test_hessian_fq_validation(lib):
     assert f(P + 2, 16, 32, 32, P, P, None, P, need, None) == ALIGN
     assert f(P, 16, 32, 32, P, P + 4, None, P, need, None) == ALIGN        # H
     assert f(P, 16, 32, 32, P, P, None, P + 8, need, None) == ALIGN        # workspace
+    assert f(P, 16, 32, 32, P, P, P + 2, P, need, None) == ALIGN           # amax
     assert f(P, 16, 32, 32, P, P, None, P, need - 1, None) == WS
     assert f(P, 0, 32, 32, P, P, None, None, 0, None) == OK                # nothing to do
     assert f(P, 0, 32, 32, None, P, None, None, 0, None) == NULL           # scale2 even when empty
@@ -202,6 +208,8 @@ def test_cast_validation(lib):
     assert c(P, P, 2, 2, 4, 64, P, None, None, None) == NULL
     assert c(None, P, 2, 2, 4, 64, P, P, None, None) == NULL
     assert c(P, P + 1, 2, 2, 4, 64, P, P, None, None) == ALIGN
+    assert c(P, P, 2, 2, 4, 64, P, P + 2, None, None) == ALIGN     # scale2_out
+    assert c(P, P, 2, 2, 4, 64, P, P, P + 4, None) == ALIGN        # fallback counts: 8-byte atomics
     assert c(P, P, 0, 2, 4, 64, P, P, None, None) == OK
 
 
@@ -218,6 +226,8 @@ def test_fp8_validation(lib):
     assert cs(None, 8, P, None, None) == NULL
     assert cs(P, 8, None, None, None) == NULL
     assert cs(P + 2, 8, P, None, None) == ALIGN
+    assert cs(P, 8, P + 2, None, None) == ALIGN            # scale_out: an atomic target
+    assert cs(P, 8, P, P + 1, None) == ALIGN               # amax_out
     q = lib.fp8e4m3_quantize
     assert q(P, 4, 12, 16, P, P, None) == SHAPE            # k % 8
     assert q(P, 4, 16, 8, P, P, None) == SHAPE             # ld < k
