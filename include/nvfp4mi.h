@@ -399,7 +399,8 @@ int nvfp4_block_hadamard(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx
 /*
  * H_out[g] = RN_f32(R_g^T H[g] R_g) for g < groups, in fp64.  H and H_out are
  * [groups][16][16] float; H_out may be H (in place), otherwise no overlap.
- * Errors: NULL_ARG, BAD_SHAPE (groups < 0), HIP.
+ * Errors: NULL_ARG, BAD_SHAPE (groups < 0), MISALIGNED (H or H_out not
+ *         4-byte aligned), HIP.
  */
 int nvfp4_hessian_hadamard(const float* H, int64_t groups, float* H_out, void* stream);
 

@@ -313,6 +313,7 @@ int nvfp4_hessian_hadamard(const float* H, int64_t groups, float* H_out, void* s
   if (groups < 0 || !mul_fits(groups, 1024)) return NVFP4_ERR_BAD_SHAPE;
   if (groups == 0) return NVFP4_OK;
   if (!H || !H_out) return NVFP4_ERR_NULL_ARG;
+  if (!aligned4(H) || !aligned4(H_out)) return NVFP4_ERR_MISALIGNED;
   return launch_hessian_hadamard(H, groups, H_out, as_stream(stream));
 }
 

@@ -264,6 +264,8 @@ def test_hadamard_validation(lib):
     assert h(P, -1, P, None) == SHAPE
     assert h(None, 4, P, None) == NULL
     assert h(P, 4, None, None) == NULL
+    assert h(P + 2, 4, P, None) == ALIGN
+    assert h(P, 4, P + 1, None) == ALIGN
     assert h(None, 0, None, None) == OK
 
 
