@@ -423,6 +423,17 @@ def main():
         rot = rotated_stage_times(lib, chk, dev, stream, sptr, W, x3, s2x3, q3, P5, E5, c5, fb, ceil)
         for k, v in rot.items():
             stage_rep[k]["rotated"] = v
+        # the read-and-write stages against a plain copy of the same number of
+        # bytes, timed the same way (a size-matched ceiling: short kernels do
+        # not reach the 2 GiB streaming rates)
+        for k in ("a4_quantize", "a5_dequant", "a6_cast"):
+            r = rot[k]
+            nbytes = r["GBps"] * 1e9 * r["ms_per_call"] / 1e3
+            cu = copy_same_bytes_us(lib, chk, dev, stream, sptr, nbytes)
+            r["copy_same_bytes_us"] = round(cu, 2)
+            # a time ratio, not a utilisation: above 1 the stage beats a 1:1 copy
+            # of its byte count (a write-heavy mix can)
+            r["copy_time_over_stage_time"] = round(cu / (r["ms_per_call"] * 1e3), 4)
         stage_rep["c2_qproj"] = c2_leg(lib, chk, dev, stream, sptr, ceil)
 
     if not args.no_extras:
@@ -679,6 +690,26 @@ def measure_ceilings(lib, chk, dev, stream, sptr, reps=5):
             "frac_of_copy_rule": "a stage that both reads and writes is also compared with copy_GBps: "
                                  "interleaved read and write streams on this device reach about the copy "
                                  "rate, not the serial read-then-write rate"}
+
+
+def copy_same_bytes_us(lib, chk, dev, stream, sptr, nbytes, nrot=8, reps=4):
+    """Microseconds of nvfp4_probe_copy moving nbytes in all (nbytes / 2 read,
+    nbytes / 2 written), rotating over nrot buffer pairs so that no call finds
+    its source in the MALL; best of four workgroup counts."""
+    import torch
+    half = (int(nbytes) // 2 + 15) // 16 * 16
+    src = [torch.zeros(half, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    best = float("inf")
+    for g in (256, 512, 1024, 2048):
+        def one(g=g):
+            for i in range(nrot):
+                chk("probe copy", lib.nvfp4_probe_copy(src[i].data_ptr(), dst[i].data_ptr(), half, g, sptr))
+        one()
+        best = min(best, ev_ms(stream, one, reps, warm=0) / nrot * 1e3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
 
 
 def ceiling_for(ceil, r, w):
