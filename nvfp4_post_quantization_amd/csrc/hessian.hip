@@ -19,8 +19,9 @@
 //    transposing reads (ds_read_b64_tr_b16); the 16-byte chunks are
 //    XOR-swizzled by row so the lane groups of a read hit disjoint banks;
 //  * a workgroup writes one fp32 partial per slab its range touches (at most
-//    a few); a second kernel adds, per group, the partials of that slab's
-//    workgroups to H in fp64, in workgroup order (deterministic).
+//    a few), one set per chunk in a chunk-list call; a second kernel adds,
+//    per group, the partials of that slab's workgroups of every chunk to H in
+//    fp64, in a fixed order (deterministic).
 // Optionally the running max |x| (calibration step 1) is taken from the MFMA
 // operands, which together hold every element of a tile.
 // The W4A4 variant (nvfp4_hessian_accum_fq) accumulates the Hessian of the
