@@ -31,7 +31,8 @@ def _check(packed, e8):
 
 @pytest.mark.parametrize("seed,experts,rows,k,frac", [(0, 4, 64, 512, 0.01), (1, 3, 16, 7168, 0.005),
                                                       (2, 2, 8, 256, 0.2),
-                                                      (3, 3, 96, 4096, 0.01)])   # 1.5 kmax steps per group
+                                                      (3, 3, 96, 4096, 0.01),    # 1.5 kmax steps per group
+                                                      (7, 3, 256, 8192, 0.01)])  # four kmax partials per group
 def test_cast_small(seed, experts, rows, k, frac):
     note(f"cast seed={seed} experts={experts} rows={rows} k={k}")
     packed, e8, forced = datagen.config5(seed=seed, experts=experts, rows=rows, k=k, forced_frac=frac)
@@ -106,3 +107,18 @@ def test_cast_many_fallbacks_per_lane():
     fb = _check(packed, e8)
     assert np.array_equal(fb, forced.reshape(2, -1).sum(axis=1))
     assert fb.min() > 0.5 * 64 * 2 * (2048 // 32)
+
+
+def test_cast_whole_chunks_with_nan_groups():
+    """Groups of whole code chunks (every codes workgroup starts on a full
+    chunk): one group with scattered NaN exponents, one with no valid
+    exponent at all."""
+    note("cast whole chunks, NaN groups")
+    rng = np.random.default_rng(8)
+    g, m, r, k = 2, 2, 64, 8192
+    packed = rng.integers(0, 256, (g, m, r, k // 2)).astype(np.uint8)
+    e8 = (127 + rng.integers(-20, 4, (g, m, r, k // 32))).astype(np.uint8)
+    e8[0, 0, 5, 7] = 255
+    e8[0, 1, 60, 200] = 255
+    e8[1] = 255
+    _check(packed, e8)
