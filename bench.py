@@ -785,7 +785,7 @@ def sweep_work_report(stats, seconds):
                       f"code slot for all 64 lanes; executed flop = 64 x (steps x {QUANT_FLOP} + full-form steps "
                       f"x {FORM_FLOP} + screen steps x {SCREEN_FLOP}), useful flop = evaluated codes x "
                       f"{QUANT_FLOP + FORM_FLOP}, against the {VALU_NONPACKED_TFLOPS} TFLOP/s non-packed fp32 VALU "
-                      f"ceiling of this build; the exhaustive roofline is the spec-peak rate of a search that "
+                      f"ceiling of the library as compiled (packed fp32 forms off); the exhaustive roofline is the spec-peak rate of a search that "
                       f"evaluates all 127 codes ({SWEEP_FLOP_PER_BLOCK} flop per block)"),
     }
     return out
