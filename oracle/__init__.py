@@ -32,8 +32,10 @@ Sources (page title, section):
 
 Readings where the pages are silent are marked "reading:" in the docstrings.
 
-Parity unpinned (readings the pages cannot confirm; no worked example is
-printed): the argmin tie-break (lowest code), the sign of a zero nibble, the
+Readings no worked example on the pages can confirm (every function is
+still pinned by the tests to closed forms, brute force, library routines
+and invariants; what stays open is only whether the pages meant these
+readings): the argmin tie-break (lowest code), the sign of a zero nibble, the
 exact-quotient rounding rule, nibble order within a byte, the clamp of a
 nonzero block's code to 0x01, the synthetic input recipes, (for the W4A4
 Hessian variant) that the layer input is taken after its activation

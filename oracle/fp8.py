@@ -18,7 +18,9 @@ Readings (the page gives no formula for the FP8 scale or rounding):
   value saturates (the encode of x / 0);
 * dequant is the one-DQ form of the pi05 flow note §5.4: RN_bf16(RN_f32(e4m3
   * s)).
-Parity unpinned: these readings (no worked example is printed).
+These are readings: no worked example on the pages confirms them.  The
+functions are pinned by tests/test_oracle_fp8.py (rational brute force,
+torch's float8_e4m3fn cast on exact quotients, invariants).
 """
 from __future__ import annotations
 

@@ -21,7 +21,9 @@ Readings (the page prints the idea, not a format):
 * the rotated sweep uses the rotated tensor's own scale_2, and its cost
   (w' - q')^T H' (w' - q') equals the Hessian-weighted error of the
   un-rotated dequantized weights q' R^T, so costs compare directly.
-Parity unpinned: these readings (no worked example is printed).
+These are readings: no worked example on the pages confirms them.  The
+functions are pinned by tests/test_oracle_rotate.py (scipy's Hadamard
+matrix, exact rational products, invariants).
 """
 from __future__ import annotations
 
