@@ -1,4 +1,4 @@
-"""The sweep's diagonal screen, checked on the CPU.
+"""The sweep's diagonal screen and its window sum bounds, checked on the CPU.
 
 The sweep kernel skips the quadratic form e^T H e for a code when
 mu2 * s > thr, with s = sum_i (e_i e_i) (H_ii / 2) in fp32, mu2 =
@@ -111,3 +111,39 @@ def test_screen_off_beyond_limit():
         h = _hessians(rng, 50, rlim)
         rmax, mu2 = _screen_factor(h)
         assert np.all(mu2[rmax > 0.9] == 0)
+
+
+def test_window_sum_bounds_are_lower_bounds():
+    """The sweep closes a window side, where the screen is on, when
+    (1 - max r) sum_i H_ii e_i^2 over the elements whose error is fixed
+    beyond that side exceeds the threshold.  Checked on exact costs (the
+    oracle's float64 cost of every code): for every code c,
+      low:  (1 - max r) sum_i H_ii (|w_i| - 6 d_c)_+^2  <= min_{c' <= c} cost(c'),
+      high: (1 - max r) sum_{|w_i| <= d_c / 4} H_ii w_i^2 <= min_{c' >= c} cost(c'),
+    on H with row sums up to the screen's limit 0.9 (bound attained for the
+    tight matrices), channel scales 1 to 40, and weights of mixed magnitude."""
+    import datagen
+    from oracle import nvfp4 as N
+    from oracle import formats as F
+    rng = np.random.default_rng(11)
+    for rmax, tight in ((0.3, False), (0.9, False), (0.9, True)):
+        h = _hessians(rng, 8, rmax, tight).astype(np.float64)            # 8 groups
+        w = rng.laplace(0.0, 1.0, (64, 8 * 16)) * np.exp(rng.uniform(-3.0, 3.0, (64, 8 * 16)))
+        bits = datagen.f32_to_bf16_bits(w.astype(np.float32))
+        _, s2 = N.tensor_scale(bits)
+        cost = N.sweep_costs(bits, h, s2)                                   # [64, 8, 127]
+        wb = np.abs(F.bf16_bits_to_f64(bits)).reshape(64, 8, 16)
+        hd = np.einsum("gii->gi", h)                                        # H_ii per group
+        isd = 1.0 / np.sqrt(hd)
+        r = (np.abs(h * isd[:, :, None] * isd[:, None, :]).sum(axis=2) - 1.0).max(axis=1)
+        mu = 1.0 - r                                                        # per group
+        d = N.block_scale(np.arange(127), s2)                               # [127]
+        low_min = np.minimum.accumulate(cost, axis=2)                       # min over c' <= c
+        high_min = np.minimum.accumulate(cost[:, :, ::-1], axis=2)[:, :, ::-1]
+        for c in range(1, 127):
+            el = np.maximum(wb - 6.0 * d[c], 0.0)
+            lb_low = mu[None, :] * np.sum(hd[None, :, :] * el * el, axis=2)
+            eh = np.where(wb <= d[c] / 4.0, wb, 0.0)
+            lb_high = mu[None, :] * np.sum(hd[None, :, :] * eh * eh, axis=2)
+            assert np.all(lb_low <= low_min[:, :, c] * (1 + 1e-12)), (rmax, c)
+            assert np.all(lb_high <= high_min[:, :, c] * (1 + 1e-12)), (rmax, c)
