@@ -171,7 +171,8 @@ int nvfp4_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t ld
  *            over all chunks).
  * workspace  16-byte aligned device buffer of at least
  *            nvfp4_hessian_chunks_workspace_bytes(tokens, k, nchunks) bytes
- *            (one chunk's plain-kernel partial slots per chunk); scratch.
+ *            (one chunk's partial slots per chunk, sized for either
+ *            chunk-list call); scratch.
  * Errors: as for nvfp4_hessian_accum, plus BAD_SHAPE for nchunks out of range
  *         and NULL_ARG for xs or a NULL chunk.
  */
@@ -225,6 +226,21 @@ int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, in
 int nvfp4_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx,
                            const float* scale2, float* H, float* amax_inout,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_hessian_accum_fq over several resident chunks in one call (the W4A4
+ * tier of "Coder390 NVFP4 校正（校准）方式" §3; the W4A4 form of
+ * nvfp4_hessian_accum_chunks): one accumulate launch per chunk
+ * into its own partial slots, one fp64 reduce over all of them.
+ * xs, nchunks, workspace (nvfp4_hessian_chunks_workspace_bytes serves both
+ * chunk-list calls), chunk lifetime: as for nvfp4_hessian_accum_chunks;
+ * scale2, H, amax_inout: as for nvfp4_hessian_accum_fq.
+ * Errors: as for nvfp4_hessian_accum_chunks, plus NULL_ARG for scale2.
+ */
+int nvfp4_hessian_accum_fq_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens,
+                                  int64_t k, int64_t ldx, const float* scale2, float* H,
+                                  float* amax_inout, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * Step 3, the Hessian-weighted block-scale sweep (fp8_scale_sweep,

@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "load", "NvFp4Error", "compute_scale2", "compute_scale2_batch", "hessian_workspace_bytes",
-    "hessian_accum", "hessian_accum_chunks", "hessian_chunks_workspace_bytes", "hessian_accum_noalloc", "hessian_accum_fq", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
+    "hessian_accum", "hessian_accum_chunks", "hessian_chunks_workspace_bytes", "hessian_accum_noalloc", "hessian_accum_fq",
+    "hessian_accum_fq_chunks", "scale_sweep", "quantize_dynamic", "dequant", "mxfp4_to_nvfp4_cast",
     "fp8_compute_scale", "fp8_quantize", "fp8_dequant", "block_hadamard", "hessian_hadamard",
     "fakequant", "quantlinear_workspace_bytes", "quantlinear_forward", "scale_sweep_stats",
 ]
@@ -47,6 +48,9 @@ _SIGS = {
                                                   _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "nvfp4_hessian_accum_fq": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                               _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "nvfp4_hessian_accum_fq_chunks": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, _i64, _i64, _i64,
+                                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t,
+                                                     _c_void_p]),
     "nvfp4_scale_sweep": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                          _c_void_p, _c_void_p, _c_void_p]),
     "nvfp4_scale_sweep_ex": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
@@ -280,6 +284,39 @@ def hessian_accum_fq(x: torch.Tensor, scale2: torch.Tensor, H: torch.Tensor, ama
     _check("nvfp4_hessian_accum_fq", load().nvfp4_hessian_accum_fq(
         x.data_ptr(), tokens, k, ldx, scale2.data_ptr(), H.data_ptr(),
         amax.data_ptr() if amax is not None else None, workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return H
+
+
+def hessian_accum_fq_chunks(xs, scale2: torch.Tensor, H: torch.Tensor, amax: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """hessian_accum_fq over up to 64 bf16 chunks of one shape [tokens, k]
+    (row-major, same row stride): one accumulate launch per chunk and one
+    reduce over all of them; in place.  amax is raised to the raw max |x|
+    over all chunks when given."""
+    xs = list(xs)
+    if not xs or len(xs) > 64:
+        raise ValueError("hessian_accum_fq_chunks takes 1 to 64 chunks")
+    for i, x in enumerate(xs):
+        _dev(x, torch.bfloat16, f"xs[{i}]", 2)
+        if x.shape != xs[0].shape or x.stride() != xs[0].stride():
+            raise ValueError("all chunks must have one shape and row stride")
+    _dev(H, torch.float32, "H")
+    _dev(scale2, torch.float32, "scale2")
+    tokens, k = xs[0].shape
+    if H.numel() != (k // 16) * 256 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [k/16, 16, 16] tensor")
+    ldx = _row_major(xs[0], "xs[0]")
+    n = len(xs)
+    need = hessian_chunks_workspace_bytes(tokens, k, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xs[0].device)
+    _dev(workspace, torch.uint8, "workspace")
+    if amax is not None:
+        _dev(amax, torch.float32, "amax")
+    ptrs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    _check("nvfp4_hessian_accum_fq_chunks", load().nvfp4_hessian_accum_fq_chunks(
+        ptrs, n, tokens, k, ldx, scale2.data_ptr(), H.data_ptr(), amax.data_ptr() if amax is not None else None,
+        workspace.data_ptr(), workspace.numel(), _stream(xs[0])))
     return H
 
 

@@ -122,15 +122,20 @@ size_t nvfp4_hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchun
   return hessian_chunks_workspace_bytes(tokens, k, nchunks);
 }
 
-int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
-                               float* H, float* amax_inout, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+// shared by both chunk-list calls; *empty is set when there is nothing to do
+static int check_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                        const float* H, const float* amax, const void* workspace, size_t workspace_bytes,
+                        bool* empty) {
+  *empty = false;
   if (nchunks < 1 || nchunks > kMaxChunks) return NVFP4_ERR_BAD_SHAPE;
   int st = check_matrix(tokens, k, ldx, 2);
   if (st) return st;
   if (k % 16) return NVFP4_ERR_BAD_SHAPE;
   if (!xs || !H) return NVFP4_ERR_NULL_ARG;
-  if (tokens == 0) return NVFP4_OK;
+  if (tokens == 0) {
+    *empty = true;
+    return NVFP4_OK;
+  }
   for (int c = 0; c < nchunks; ++c) {
     if (!xs[c]) return NVFP4_ERR_NULL_ARG;
     if ((st = check_bf16_rows(xs[c], ldx))) return st;
@@ -139,8 +144,29 @@ int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t t
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (!workspace) return NVFP4_ERR_NULL_ARG;
   if (!aligned16(H) || !aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
-  if (amax_inout && !aligned4(amax_inout)) return NVFP4_ERR_MISALIGNED;
+  if (amax && !aligned4(amax)) return NVFP4_ERR_MISALIGNED;                                   // atomic target
+  return NVFP4_OK;
+}
+
+int nvfp4_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                               float* H, float* amax_inout, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  bool empty = false;
+  const int st = check_chunks(xs, nchunks, tokens, k, ldx, H, amax_inout, workspace, workspace_bytes, &empty);
+  if (st || empty) return st;
   return launch_hessian_accum_chunks(xs, nchunks, tokens, k, ldx, H, amax_inout, workspace, as_stream(stream));
+}
+
+int nvfp4_hessian_accum_fq_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                                  const float* scale2, float* H, float* amax_inout, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  const int st = check_chunks(xs, nchunks, tokens, k, ldx, H, amax_inout, workspace, workspace_bytes, &empty);
+  if (st) return st;
+  if (!scale2) return NVFP4_ERR_NULL_ARG;
+  if (empty) return NVFP4_OK;
+  return launch_hessian_accum_fq_chunks(xs, nchunks, tokens, k, ldx, scale2, H, amax_inout, workspace,
+                                        as_stream(stream));
 }
 
 int nvfp4_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, float* H,

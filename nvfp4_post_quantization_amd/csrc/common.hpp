@@ -54,6 +54,8 @@ constexpr int kMaxChunks = 64;           // chunks per nvfp4_hessian_accum_chunk
 int launch_hessian_accum_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
                                 float* H, float* amax, void* workspace, hipStream_t s);
 size_t hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchunks);
+int launch_hessian_accum_fq_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                                   const float* scale2, float* H, float* amax, void* workspace, hipStream_t s);
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
                             float* amax, void* workspace, hipStream_t s);
 int launch_fp8_scale(const uint16_t* x, int64_t n, float* scale_out, float* amax_out, hipStream_t s);

@@ -510,8 +510,10 @@ int launch_hessian_accum(const uint16_t* x, int64_t tokens, int64_t k, int64_t l
   return launch_hessian_accum_chunks(&x, 1, tokens, k, ldx, H, amax, workspace, s);
 }
 
+// one query for both chunk-list calls: the larger of the two per-chunk slot
+// sets, times the chunk count
 size_t hessian_chunks_workspace_bytes(int64_t tokens, int64_t k, int nchunks) {
-  return plan_bytes(plan(tokens, k, kTargetWgs, kPlainSG)) * (size_t)nchunks;
+  return hessian_workspace_bytes(tokens, k) * (size_t)nchunks;
 }
 
 size_t hessian_plain_workspace_bytes(int64_t tokens, int64_t k) {
@@ -551,16 +553,28 @@ int launch_hessian_accum_noalloc(const uint16_t* x, int64_t tokens, int64_t k, i
   return launch_hessian_accum(x, tokens, k, ldx, H, amax, ws, s);
 }
 
+int launch_hessian_accum_fq_chunks(const uint16_t* const* xs, int nchunks, int64_t tokens, int64_t k, int64_t ldx,
+                                   const float* scale2, float* H, float* amax, void* workspace, hipStream_t s) {
+  const Plan p = plan(tokens, k, kTargetWgsFq, kFqSG);
+  if (p.wgs == 0 || nchunks == 0) return NVFP4_OK;
+  // as the plain chunk list: one accumulate launch per chunk into its own
+  // partial slot set, one fp64 reduce over all of them
+  float* ws = static_cast<float*>(workspace);
+  const int64_t chunk_floats = p.wgs * p.segs * kFqSG * 256;
+  const int fx = force_exact_flag();
+  for (int c = 0; c < nchunks; ++c) {
+    hessian_fq_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(xs[c], tokens, k, ldx, p.tiles, p.total, p.wgs,
+                                                                    p.segs, p.slabs, p.streams, ws + c * chunk_floats,
+                                                                    amax, scale2, fx);
+    const int st = launch_status("hessian_fq_partial_kernel");
+    if (st) return st;
+  }
+  return launch_reduce<kFqSG>(p, k, ws, H, s, nchunks);
+}
+
 int launch_hessian_accum_fq(const uint16_t* x, int64_t tokens, int64_t k, int64_t ldx, const float* scale2, float* H,
                             float* amax, void* workspace, hipStream_t s) {
-  const Plan p = plan(tokens, k, kTargetWgsFq, kFqSG);
-  if (p.wgs == 0) return NVFP4_OK;
-  float* ws = static_cast<float*>(workspace);
-  hessian_fq_partial_kernel<<<(unsigned)p.wgs, kThreads, 0, s>>>(x, tokens, k, ldx, p.tiles, p.total, p.wgs, p.segs,
-                                                                  p.slabs, p.streams, ws, amax, scale2,
-                                                                  force_exact_flag());
-  int st = launch_status("hessian_fq_partial_kernel");
-  return st ? st : launch_reduce<kFqSG>(p, k, ws, H, s);
+  return launch_hessian_accum_fq_chunks(&x, 1, tokens, k, ldx, scale2, H, amax, workspace, s);
 }
 
 }  // namespace nvfp4

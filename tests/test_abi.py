@@ -40,7 +40,8 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "nvfp4_status_string", "nvfp4_compute_scale2", "nvfp4_compute_scale2_batch", "nvfp4_hessian_workspace_bytes",
         "nvfp4_hessian_accum", "nvfp4_hessian_accum_noalloc", "nvfp4_hessian_accum_fq",
-        "nvfp4_hessian_chunks_workspace_bytes", "nvfp4_hessian_accum_chunks", "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
+        "nvfp4_hessian_chunks_workspace_bytes", "nvfp4_hessian_accum_chunks", "nvfp4_hessian_accum_fq_chunks",
+        "nvfp4_scale_sweep", "nvfp4_quantize_dynamic", "nvfp4_dequant",
         "mxfp4_to_nvfp4_cast", "fp8e4m3_compute_scale", "fp8e4m3_quantize", "fp8e4m3_dequant",
         "nvfp4_block_hadamard", "nvfp4_hessian_hadamard", "nvfp4_fakequant", "nvfp4_scale_sweep_ex",
         "nvfp4_quantlinear_workspace_bytes", "nvfp4_quantlinear_forward",
@@ -140,6 +141,17 @@ def test_hessian_chunks_validation(lib):
     assert f(xs, 2, 16, 32, 32, P, None, P + 8, need, None) == ALIGN        # workspace
     assert f(xs, 2, 16, 32, 32, P, P + 2, P, need, None) == ALIGN           # amax
     assert f(xs, 2, 0, 32, 32, P, None, None, 0, None) == OK                # nothing to do
+    fq = lib.nvfp4_hessian_accum_fq_chunks
+    assert fq(xs, 0, 16, 32, 32, P, P, None, P, need, None) == SHAPE          # nchunks < 1
+    assert fq(xs, 2, 16, 24, 24, P, P, None, P, need, None) == SHAPE          # k % 16
+    assert fq(xs, 2, 16, 32, 32, None, P, None, P, need, None) == NULL        # scale2
+    assert fq(xs, 2, 16, 32, 32, P, None, None, P, need, None) == NULL        # H
+    assert fq(bad, 2, 16, 32, 32, P, P, None, P, need, None) == NULL          # a NULL chunk
+    assert fq(mis, 2, 16, 32, 32, P, P, None, P, need, None) == ALIGN
+    assert fq(xs, 2, 16, 32, 32, P, P, None, P, need - 1, None) == WS
+    assert fq(xs, 2, 16, 32, 32, P, P, P + 2, P, need, None) == ALIGN         # amax
+    assert fq(xs, 2, 0, 32, 32, P, P, None, None, 0, None) == OK              # nothing to do
+    assert fq(xs, 2, 0, 32, 32, None, P, None, None, 0, None) == NULL         # scale2 even when empty
 
 
 def test_hessian_noalloc_validation(lib):

@@ -202,3 +202,31 @@ def test_fq_wide_k_ranges_cross_slabs(t, k):
     rng = np.random.default_rng(t * k)
     x = datagen.f32_to_bf16_bits(rng.laplace(0, 1, (t, k)).astype(np.float32))
     _check(x)
+
+
+@pytest.mark.parametrize("t,k,chunks", [(1000, 272, 3), (4096, 2048, 5), (64, 512, 64)])
+def test_fq_chunk_list(path, t, k, chunks):
+    """Several chunks in one W4A4 call: H against the oracle over all chunks'
+    tokens, bitwise reproducible, the raw amax over every chunk, and within
+    the bound of the per-chunk calls."""
+    note(f"hessian_fq chunk list t={t} k={k} chunks={chunks} path={path}")
+    rng = np.random.default_rng(t + k + chunks)
+    bits = [datagen.f32_to_bf16_bits(rng.laplace(0, 1, (t, k)).astype(np.float32)) for _ in range(chunks)]
+    allbits = np.concatenate(bits, axis=0)
+    s2 = N.tensor_scale(allbits)[1]
+    xs = [to_dev_bf16(b) for b in bits]
+    s2_dev = to_dev_f32([s2])
+    runs = []
+    for _ in range(2):
+        H = torch.zeros((k // 16, 16, 16), dtype=torch.float32, device=DEV)
+        amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+        nq.hessian_accum_fq_chunks(xs, s2_dev, H, amax)
+        runs.append((host(H), float(host(amax)[0])))
+    assert np.array_equal(runs[0][0], runs[1][0]), "chunk-list accumulation must be bitwise reproducible"
+    ref = N.hessian_fakequant(allbits, s2)
+    assert rel_frobenius(runs[0][0], ref).max() <= TOL
+    assert runs[0][1] == float(np.max(np.abs(F.bf16_bits_to_f64(allbits))))
+    Hs = torch.zeros((k // 16, 16, 16), dtype=torch.float32, device=DEV)
+    for x in xs:
+        nq.hessian_accum_fq(x, s2_dev, Hs)
+    assert rel_frobenius(host(Hs), ref).max() <= TOL
